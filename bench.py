@@ -1,0 +1,164 @@
+"""Benchmark: one batched speculative-sampling verification step per timed step.
+
+Workload: B=64 rows, gamma=8 draft tokens, V=128256, bf16 Zipf-shaped logits
+(ranks permuted per row, per-row temperature in {0.1, 0.4, 0.7, 1.0}); draft =
+target + N(0, 1). Synthetic, seeded, generated on the host then copied to HBM
+before timing.
+
+Prints one JSON line: verified draft tokens/s (B*gamma per step) and the HBM
+roofline of the dominant kernel, plus the fp64 CPU oracle timed on a bounded
+sample as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--copies C] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import device_draft_verification_specverify_amd as sv  # noqa: E402
+import workloads  # noqa: E402
+
+METRIC = "verified draft tokens/s + HBM GB/s (% of peak) at B=64, γ=8, V=128256 bf16"
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(w) -> int:
+    """Every logit the rule needs, read once, plus tokens, temperatures and outputs."""
+    e = w.bytes_per_logit
+    sampled = int((w.temperature > 0).sum())
+    logits = w.B * (w.gamma + 1) * w.V * e + sampled * w.K * w.gamma * w.V * e
+    scalars = w.B * w.K * w.gamma * 4 + w.B * 4 + w.B * 8 + 2 * w.B * w.K * 4
+    return logits + scalars
+
+
+def stacked_inputs(w, dev):
+    """Target and draft rows of one copy in a single [B, 2*gamma+1, V] buffer; returns views."""
+    raw = np.concatenate([w.target, w.draft[:, 0]], axis=1)
+    buf = torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+    g = w.gamma
+    return buf, buf[:, : g + 1], buf[:, g + 1:].unsqueeze(1)
+
+
+def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 3) -> dict:
+    import oracle
+
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        oracle.verify(w.target, w.draft, w.tokens, w.temperature, w.seed, w.pos0, dtype=w.dtype)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": w.B * w.K * w.gamma / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full step(s) of the benchmark workload ({w.B} chains, "
+                      f"{w.B * w.K * w.gamma} draft tokens), NumPy float64, single thread",
+            "seconds_per_step": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4,
+                    help="input copies cycled so consecutive steps never reuse cached logits")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verification path runs on a single device "
+              "(sharding is described, not built); use --gpus 1", file=sys.stderr)
+        return 2
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.make("c3")
+    copies = []
+    for c in range(args.copies):
+        buf, tgt, dft = stacked_inputs(w, dev)
+        copies.append((buf, tgt, dft))
+    tokens = torch.from_numpy(w.tokens).to(dev)
+    temp = torch.from_numpy(w.temperature).to(dev)
+    pos0 = torch.from_numpy(w.pos0).to(dev)
+    plans = [sv.StepPlan(t, d, tokens, temp, w.seed, pos0) for (_, t, d) in copies]
+    stream = torch.cuda.current_stream(dev)
+
+    for i in range(args.warmup):
+        plans[i % len(plans)]()
+    torch.cuda.synchronize(dev)
+
+    # Timed region: exactly `steps` steps, bracketed by device synchronisation.
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plans[i % len(plans)]()
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+
+    # Dominant kernel: the streaming normaliser over the same 1088 rows, timed with
+    # HIP events on the launch stream (the normalise entry point launches it plus a
+    # one-thread-per-row finalise).
+    ws = sv.workspace(w.B, 0, 2 * w.gamma, w.V, sv.SV_BF16, dev)
+    temp_rows = temp
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.warmup):
+        sv.specverify_normalize(copies[i % len(copies)][0], temp_rows, ws=ws)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        sv.specverify_normalize(copies[i % len(copies)][0], temp_rows, ws=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    out = plans[0].out
+    err = int(out.device_error.item())
+    bytes_min = algorithmic_bytes(w)
+    kernel_bytes = w.B * (2 * w.gamma + 1) * w.V * w.bytes_per_logit
+    achieved = kernel_bytes / (kern_ms * 1e-3) / 1e9
+    tokens_per_step = w.B * w.K * w.gamma
+    value = tokens_per_step / (ms_per_step * 1e-3)
+    step_gbps = bytes_min / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "B=64, gamma=8, V=128256 bf16 Zipf logits, per-row T in "
+                               "{0.1,0.4,0.7,1.0}, K=1", "B": w.B, "K": w.K, "gamma": w.gamma,
+                   "V": w.V, "logits": "bf16", "input_copies_cycled": args.copies},
+        "hbm_gbps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+        "bytes_min_per_step": bytes_min,
+        "accepted_tokens_per_step": int((out.accept_len.clamp(min=0) + 1).sum().item()),
+        "device_error": err,
+        "roofline": {"bound": "hbm", "kernel": "rowstats_kernel (+finalize_rows_kernel)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": kernel_bytes, "avg_launch_ms": kern_ms},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,256 @@
+"""Python binding of libspecverify: batched speculative-sampling verification on MI355X.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels of ``libspecverify.so``; torch supplies device memory and the stream.
+The functions carry the C ABI's names (see include/specverify.h) and raise if
+the library has not been built -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libspecverify.so")
+
+SV_F32 = 0
+SV_BF16 = 1
+SV_OK = 0
+SV_ERR_TOKEN = 1
+SV_ERR_TEMP = 2
+SV_ERR_ROW = 4
+MAX_GAMMA = 32
+MAX_CHAIN_DECISIONS = 64
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "specverify_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
+    "specverify_normalize": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "specverify_accept": (_INT, [_P, _P, _I64, _I64, _I64, _U64, _P, _P, _P, _P]),
+    "specverify_residual_sample": (_INT, [_P, _P, _INT, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                          _I64, _I64, _P, _P, _P, _P, _P, _U64, _P, _P, _P, _SZ,
+                                          _P]),
+    "specverify_step": (_INT, [_P, _P, _INT, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                               _I64, _P, _U64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "specverify_status_string": (ctypes.c_char_p, [_INT]),
+    "specverify_version": (_INT, []),
+}
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libspecverify.so (built by __graft_entry__.build()); raises if missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise SpecVerifyError(f"{path} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != SV_OK:
+        msg = load_library().specverify_status_string(status).decode()
+        raise SpecVerifyError(f"{what}: status {status} ({msg})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise SpecVerifyError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, shape: tuple, name: str) -> None:
+    if not t.is_cuda:
+        raise SpecVerifyError(f"{name} must be a device tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise SpecVerifyError(f"{name}: want contiguous {dtype} {tuple(shape)}, got {t.dtype} "
+                              f"{tuple(t.shape)} contiguous={t.is_contiguous()}")
+
+
+def _logits(t: torch.Tensor, ndim: int, name: str) -> None:
+    if not t.is_cuda or t.dim() != ndim or t.stride(-1) != 1:
+        raise SpecVerifyError(f"{name}: want a {ndim}-d device tensor with a contiguous last axis")
+
+
+def workspace_size(B: int, K: int, gamma: int, V: int, dtype: int) -> int:
+    return int(load_library().specverify_workspace_size(B, K, gamma, V, dtype))
+
+
+def workspace(B: int, K: int, gamma: int, V: int, dtype: int, device) -> torch.Tensor:
+    n = workspace_size(B, K, gamma, V, dtype)
+    if n == 0:
+        raise SpecVerifyError("sizes rejected by specverify_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def specverify_normalize(logits: torch.Tensor, temperature: torch.Tensor, want_argmax: bool = False,
+                         ws: torch.Tensor | None = None):
+    """lnZ [B, P] float64 (and argmax [B, P] int32) of logits [B, P, V]."""
+    lib = load_library()
+    _logits(logits, 3, "logits")
+    B, P, V = logits.shape
+    _need(temperature, torch.float32, (B,), "temperature")
+    dt = _dtype_code(logits)
+    lnz = torch.empty((B, P), dtype=torch.float64, device=logits.device)
+    am = torch.empty((B, P), dtype=torch.int32, device=logits.device) if want_argmax else None
+    if ws is None:
+        ws = workspace(B, 0, P - 1, V, dt, logits.device)
+    st = lib.specverify_normalize(logits.data_ptr(), dt, B, P, V, logits.stride(0), logits.stride(1),
+                                  temperature.data_ptr(), lnz.data_ptr(), _ptr(am), ws.data_ptr(),
+                                  ws.numel(), _stream(logits.device))
+    _check(st, "specverify_normalize")
+    return lnz, am
+
+
+def specverify_accept(logp: torch.Tensor, logq: torch.Tensor, seed: int, pos0: torch.Tensor | None = None,
+                      want_bits: bool = False):
+    """accept_len [B, K] int32 (and accept_bits [B, K] int32 view of uint32) from ln p/ln q [B, K, gamma]."""
+    lib = load_library()
+    B, K, g = logp.shape
+    _need(logp, torch.float32, (B, K, g), "logp")
+    _need(logq, torch.float32, (B, K, g), "logq")
+    if pos0 is not None:
+        _need(pos0, torch.int64, (B,), "pos0")
+    n = torch.empty((B, K), dtype=torch.int32, device=logp.device)
+    bits = torch.empty((B, K), dtype=torch.int32, device=logp.device) if want_bits else None
+    st = lib.specverify_accept(logp.data_ptr(), logq.data_ptr(), B, K, g, seed & (2 ** 64 - 1),
+                               _ptr(pos0), n.data_ptr(), _ptr(bits), _stream(logp.device))
+    _check(st, "specverify_accept")
+    return n, bits
+
+
+def specverify_residual_sample(target: torch.Tensor, draft: torch.Tensor, temperature: torch.Tensor,
+                               lnZ_target: torch.Tensor, lnZ_draft: torch.Tensor,
+                               argmax_target: torch.Tensor, accept_len: torch.Tensor, seed: int,
+                               pos0: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """out_token [B, K] int32 given the accept lengths (see the C header)."""
+    lib = load_library()
+    _logits(target, 3, "target")
+    _logits(draft, 4, "draft")
+    B, G1, V = target.shape
+    K, g = draft.shape[1], draft.shape[2]
+    if G1 != g + 1 or draft.shape[0] != B or draft.shape[3] != V or draft.dtype != target.dtype:
+        raise SpecVerifyError("target [B, gamma+1, V] and draft [B, K, gamma, V] disagree")
+    _need(temperature, torch.float32, (B,), "temperature")
+    _need(lnZ_target, torch.float64, (B, g + 1), "lnZ_target")
+    _need(lnZ_draft, torch.float64, (B, K, g), "lnZ_draft")
+    _need(argmax_target, torch.int32, (B, g + 1), "argmax_target")
+    _need(accept_len, torch.int32, (B, K), "accept_len")
+    if pos0 is not None:
+        _need(pos0, torch.int64, (B,), "pos0")
+    dt = _dtype_code(target)
+    out = torch.empty((B, K), dtype=torch.int32, device=target.device)
+    if ws is None:
+        ws = workspace(B, K, g, V, dt, target.device)
+    st = lib.specverify_residual_sample(
+        target.data_ptr(), draft.data_ptr(), dt, B, K, g, V, target.stride(0), target.stride(1),
+        draft.stride(0), draft.stride(1), draft.stride(2), temperature.data_ptr(),
+        lnZ_target.data_ptr(), lnZ_draft.data_ptr(), argmax_target.data_ptr(), accept_len.data_ptr(),
+        seed & (2 ** 64 - 1), _ptr(pos0), out.data_ptr(), ws.data_ptr(), ws.numel(),
+        _stream(target.device))
+    _check(st, "specverify_residual_sample")
+    return out
+
+
+@dataclass
+class StepOutputs:
+    accept_len: torch.Tensor       # [B, K] int32
+    out_token: torch.Tensor        # [B, K] int32
+    logp: torch.Tensor | None      # [B, K, gamma] float32
+    logq: torch.Tensor | None      # [B, K, gamma] float32
+    lnZ_target: torch.Tensor | None  # [B, gamma+1] float64
+    lnZ_draft: torch.Tensor | None   # [B, K, gamma] float64
+    device_error: torch.Tensor | None  # [1] int32
+
+
+class StepPlan:
+    """Binds the tensors of one verification step once; each call enqueues the step.
+
+    target [B, gamma+1, V] and draft [B, K, gamma, V] (float32 or bfloat16, last
+    axis contiguous, any non-negative strides), tokens [B, K, gamma] int32,
+    temperature [B] float32, pos0 [B] int64 or None. Outputs are allocated here.
+    """
+
+    def __init__(self, target, draft, tokens, temperature, seed: int, pos0=None, *,
+                 want_logprobs: bool = True, want_normalizers: bool = True,
+                 want_error: bool = True, ws: torch.Tensor | None = None):
+        self.lib = load_library()
+        _logits(target, 3, "target")
+        _logits(draft, 4, "draft")
+        B, G1, V = target.shape
+        K, g = draft.shape[1], draft.shape[2]
+        if G1 != g + 1 or draft.shape[0] != B or draft.shape[3] != V or draft.dtype != target.dtype:
+            raise SpecVerifyError("target [B, gamma+1, V] and draft [B, K, gamma, V] disagree")
+        _need(tokens, torch.int32, (B, K, g), "tokens")
+        _need(temperature, torch.float32, (B,), "temperature")
+        if pos0 is not None:
+            _need(pos0, torch.int64, (B,), "pos0")
+        dev = target.device
+        self.B, self.K, self.gamma, self.V = B, K, g, V
+        self.dtype = _dtype_code(target)
+        self.target, self.draft, self.tokens, self.temperature, self.pos0 = (
+            target, draft, tokens, temperature, pos0)
+        self.seed = seed & (2 ** 64 - 1)
+        self.out = StepOutputs(
+            accept_len=torch.empty((B, K), dtype=torch.int32, device=dev),
+            out_token=torch.empty((B, K), dtype=torch.int32, device=dev),
+            logp=torch.empty((B, K, g), dtype=torch.float32, device=dev) if want_logprobs else None,
+            logq=torch.empty((B, K, g), dtype=torch.float32, device=dev) if want_logprobs else None,
+            lnZ_target=(torch.empty((B, g + 1), dtype=torch.float64, device=dev)
+                        if want_normalizers else None),
+            lnZ_draft=(torch.full((B, K, g), float("nan"), dtype=torch.float64, device=dev)
+                       if want_normalizers else None),
+            device_error=torch.zeros(1, dtype=torch.int32, device=dev) if want_error else None,
+        )
+        self.ws = ws if ws is not None else workspace(B, K, g, V, self.dtype, dev)
+        o = self.out
+        self._args = (
+            target.data_ptr(), draft.data_ptr(), self.dtype, tokens.data_ptr(), B, K, g, V,
+            target.stride(0), target.stride(1), draft.stride(0), draft.stride(1), draft.stride(2),
+            temperature.data_ptr(), self.seed, _ptr(pos0), o.accept_len.data_ptr(),
+            o.out_token.data_ptr(), _ptr(o.logp), _ptr(o.logq), _ptr(o.lnZ_target),
+            _ptr(o.lnZ_draft), _ptr(o.device_error), self.ws.data_ptr(), self.ws.numel())
+        self.device = dev
+
+    def __call__(self, stream: int | None = None) -> StepOutputs:
+        st = self.lib.specverify_step(*self._args, _stream(self.device) if stream is None else stream)
+        _check(st, "specverify_step")
+        return self.out
+
+
+def specverify_step(target, draft, tokens, temperature, seed: int, pos0=None, **kw) -> StepOutputs:
+    """One fused verification step (allocates its outputs and workspace)."""
+    return StepPlan(target, draft, tokens, temperature, seed, pos0, **kw)()
+
+
+def version() -> int:
+    return int(load_library().specverify_version())

@@ -1,0 +1,198 @@
+/*
+ * specverify.h -- batched speculative-sampling verification on AMD Instinct
+ * MI355X (gfx950), as a C ABI.
+ *
+ * The operation (the pages' shared hot path): a target model scores the
+ * gamma draft tokens of every row in one pass and the verifier accepts or
+ * rejects them token by token, on the device, without a round trip to the
+ * host ("FlashSpec: Adaptive Speculative Decoding with Online Bandit Draft
+ * Selection and Triton-Optimised Verification" -- technical summary, problem
+ * definition and section 1 "On-device verification kernel"). Temperature is
+ * applied to the logits before the log-softmax (same section, numerical
+ * stability). At the first rejection the correction token is drawn from the
+ * residual max(p - q, 0) ("Speculative Speculative Decoding" -- technical
+ * summary, section 2, optimisation 2 "Saguaro sampling"); when every draft is
+ * accepted a bonus token is drawn from the target's next distribution
+ * ("SpecTr-GBV: Multi-Draft Block Verification Accelerating Speculative
+ * Decoding" -- section 2, algorithm procedure, termination step).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless marked host. The caller owns every
+ *   buffer; the library never allocates, frees or synchronises. All work is
+ *   enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *   returns without waiting for it.
+ * - Argument errors are detected on the host before anything is enqueued and
+ *   return a negative status; no partial work is launched.
+ * - Logits are row-major with the vocabulary axis contiguous (stride 1);
+ *   other strides are in elements, must be >= 0, and may be 0 (broadcast).
+ *   Target and draft logits share one dtype (SV_F32 or SV_BF16). Rows whose
+ *   start is 16-byte aligned take 128-bit loads; other rows take element
+ *   loads (slower, same results).
+ * - Random numbers: a Philox4x32-10 stream (Salmon et al., SC'11) keyed by
+ *   (seed mod 2^32, seed >> 32) with counter (c0, position, chain row,
+ *   purpose), where chain row r = b*K + k and position = pos0[b] + j
+ *   (mod 2^32). The accept uniform of position j is word 0 of block
+ *   (0, pos0[b]+j, r, 0); the sampling noise of vocabulary id v is word v&3
+ *   of block (v>>2, pos0[b]+n, r, 1). A word w maps to
+ *   u = (floor(w / 2^9) + 1/2) * 2^-23, strictly inside (0, 1).
+ * - A temperature of exactly 0 marks a greedy row: tokens are accepted iff
+ *   they equal the target row's argmax (lowest id on ties), nothing random is
+ *   drawn, and draft logits are never read.
+ * - Results are bit-deterministic: reductions merge in a fixed order and no
+ *   floating-point atomics are used.
+ * - `workspace` is device scratch of at least specverify_workspace_size()
+ *   bytes, 256-byte aligned. It needs no initialisation and its contents are
+ *   undefined between calls; one buffer serves any number of calls ordered
+ *   on one stream, and calls that overlap in time on one buffer race.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Logit storage types. */
+#define SV_F32 0
+#define SV_BF16 1
+
+/* Return status of every entry point. */
+#define SV_OK 0
+#define SV_EINVAL (-1)     /* null pointer, size or stride out of range      */
+#define SV_EDTYPE (-2)     /* unknown logit dtype                            */
+#define SV_EWORKSPACE (-3) /* workspace missing or smaller than required     */
+#define SV_EALIGN (-4)     /* workspace not 256-byte aligned                 */
+#define SV_EHIP (-5)       /* a kernel launch failed                         */
+
+/* Bits OR-ed into the optional device error word; the chain's accept_len and
+ * out_token are set to -1 when any of them applies to it. */
+#define SV_ERR_TOKEN 1     /* a draft token outside [0, V)                   */
+#define SV_ERR_TEMP 2      /* temperature negative or NaN                    */
+#define SV_ERR_ROW 4       /* a needed row whose largest logit is -inf (all
+                              entries masked) or NaN                         */
+
+/* Size limits checked on the host. */
+#define SV_MAX_GAMMA 32
+#define SV_MAX_CHAIN_DECISIONS 64 /* K * gamma per batch row */
+
+/*
+ * Bytes of workspace that specverify_step / specverify_normalize /
+ * specverify_residual_sample need for these sizes (the largest of the three;
+ * for specverify_normalize pass K = 0 and gamma = P - 1). Pure host function.
+ * Returns 0 for sizes the library rejects.
+ */
+size_t specverify_workspace_size(int64_t B, int64_t K, int64_t gamma, int64_t V, int dtype);
+
+/*
+ * Row normalisers (FlashSpec technical summary, section 1: temperature is
+ * applied before the log-softmax; arithmetic in log space).
+ *   logits       [B, P, V] rows at logits + b*stride_b + p*stride_p (elements)
+ *   temperature  [B] float
+ *   lnZ          [B, P] double out: ln sum_v exp(z_v / T_b) for T_b > 0;
+ *                max_v z_v for T_b == 0 (the T -> 0 limit of T * ln Z);
+ *                NaN for T_b < 0 or NaN. An all -inf row gives -inf.
+ *   argmax       [B, P] int32 out, or NULL: lowest id of the row maximum of
+ *                the raw logits, for every row.
+ * Status: SV_EINVAL (null logits/temperature/lnZ, B/P/V < 1, V >= 2^31,
+ * negative stride), SV_EDTYPE, SV_EWORKSPACE, SV_EALIGN, SV_EHIP.
+ */
+int specverify_normalize(const void* logits, int dtype, int64_t B, int64_t P, int64_t V,
+                         int64_t stride_b, int64_t stride_p, const float* temperature,
+                         double* lnZ, int32_t* argmax, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Scalar-only accept test (FlashSpec technical summary, section 1 mechanism:
+ * the kernel reads two log-probability scalars per candidate, so no pass over
+ * the vocabulary is needed).
+ *   logp, logq   [B, K, gamma] float: ln p and ln q at each draft token.
+ *                A greedy row is encoded ln p in {0, -inf}, ln q = 0.
+ *   pos0         [B] int64 or NULL (all 0)
+ *   accept_len   [B, K] int32 out: number of leading accepts, where position
+ *                j accepts iff ln u_j < ln p_j - ln q_j (a NaN difference
+ *                rejects).
+ *   accept_bits  [B, K] uint32 out or NULL: bit j = decision at position j
+ *                (every position is decided, also after the first rejection).
+ * Status: SV_EINVAL (null pointers, B/K < 1, gamma outside [1, 32]), SV_EHIP.
+ */
+int specverify_accept(const float* logp, const float* logq, int64_t B, int64_t K, int64_t gamma,
+                      uint64_t seed, const int64_t* pos0, int32_t* accept_len,
+                      uint32_t* accept_bits, void* stream);
+
+/*
+ * The emitted token of every chain given its accept length (Speculative
+ * Speculative Decoding, technical summary section 2, optimisation 2: residual
+ * r proportional to max(p_target - p_draft, 0); SpecTr-GBV section 2,
+ * termination step: residual at a rejection, target sample when the whole
+ * block is accepted).
+ *   target_logits [B, gamma+1, V], draft_logits [B, K, gamma, V] (strides as named)
+ *   temperature   [B] float
+ *   lnZ_target    [B, gamma+1] double, lnZ_draft [B, K, gamma] double: the
+ *                 normalisers of specverify_normalize
+ *   argmax_target [B, gamma+1] int32: used for greedy rows (T == 0)
+ *   accept_len    [B, K] int32 in: n in [0, gamma]; chains with n < 0 are skipped
+ *   out_token     [B, K] int32 out:
+ *                 T > 0, n < gamma : argmax_v ln max(p_n - q_n, 0)(v) + G_v
+ *                 T > 0, n = gamma : argmax_v z_t[gamma, v] / T + G_v
+ *                 T = 0            : argmax_target[b, n]
+ *                 with G_v standard Gumbel noise (ties to the lowest id). If
+ *                 the residual support is empty (possible only by rounding)
+ *                 the token is drawn from p_n with the same noise.
+ * Status: as specverify_step.
+ */
+int specverify_residual_sample(const void* target_logits, const void* draft_logits, int dtype,
+                               int64_t B, int64_t K, int64_t gamma, int64_t V,
+                               int64_t t_stride_b, int64_t t_stride_j,
+                               int64_t d_stride_b, int64_t d_stride_k, int64_t d_stride_j,
+                               const float* temperature, const double* lnZ_target,
+                               const double* lnZ_draft, const int32_t* argmax_target,
+                               const int32_t* accept_len, uint64_t seed, const int64_t* pos0,
+                               int32_t* out_token, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * One fused verification step for B rows x K draft branches (all branches of
+ * row b share its target rows; each branch is its own token-level chain).
+ *   target_logits  [B, gamma+1, V]; row j verifies draft token j, row gamma
+ *                  supplies the bonus token
+ *   draft_logits   [B, K, gamma, V]
+ *   draft_tokens   [B, K, gamma] int32
+ *   temperature    [B] float (T == 0: greedy row)
+ *   seed, pos0     random stream key and [B] int64 positions (pos0 may be NULL)
+ *   accept_len     [B, K] int32 out: n = number of leading accepted drafts
+ *   out_token      [B, K] int32 out: correction (n < gamma) or bonus (n = gamma)
+ *                  token; the chain emits draft_tokens[b,k,0:n] then out_token
+ *   logp, logq     [B, K, gamma] float out or NULL: ln p, ln q at the draft
+ *                  tokens (greedy rows: ln p in {0, -inf}, ln q = 0)
+ *   lnZ_target     [B, gamma+1] double out or NULL (as specverify_normalize)
+ *   lnZ_draft      [B, K, gamma] double out or NULL (not written for greedy rows)
+ *   device_error   one int32 out or NULL: OR of SV_ERR_* bits (only set, never
+ *                  cleared: zero it before the call)
+ * Status: SV_EINVAL (null required pointer, B/K/V < 1, gamma outside [1, 32],
+ * K*gamma > 64, V >= 2^31, negative stride), SV_EDTYPE, SV_EWORKSPACE,
+ * SV_EALIGN, SV_EHIP.
+ */
+int specverify_step(const void* target_logits, const void* draft_logits, int dtype,
+                    const int32_t* draft_tokens, int64_t B, int64_t K, int64_t gamma, int64_t V,
+                    int64_t t_stride_b, int64_t t_stride_j,
+                    int64_t d_stride_b, int64_t d_stride_k, int64_t d_stride_j,
+                    const float* temperature, uint64_t seed, const int64_t* pos0,
+                    int32_t* accept_len, int32_t* out_token, float* logp, float* logq,
+                    double* lnZ_target, double* lnZ_draft, int32_t* device_error,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static host string describing a status code. */
+const char* specverify_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int specverify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,108 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+symbol its header declares, sizes workspaces, and rejects bad arguments before
+touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import device_draft_verification_specverify_amd as sv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "specverify.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sv.LIBRARY),
+                                reason="libspecverify.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(specverify_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = sv.load_library()
+    names = declared_functions()
+    assert set(names) == {"specverify_workspace_size", "specverify_normalize", "specverify_accept",
+                          "specverify_residual_sample", "specverify_step",
+                          "specverify_status_string", "specverify_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(sv._SIGNATURES)
+
+
+def test_version_and_status_strings():
+    lib = sv.load_library()
+    assert lib.specverify_version() >= 100
+    for code in (0, -1, -2, -3, -4, -5, 99):
+        assert lib.specverify_status_string(code)
+
+
+def test_workspace_sizes():
+    lib = sv.load_library()
+    c3 = lib.specverify_workspace_size(64, 1, 8, 128256, 1)
+    assert c3 > 0 and c3 % 256 == 0
+    assert lib.specverify_workspace_size(512, 4, 8, 128256, 1) > c3
+    assert lib.specverify_workspace_size(64, 0, 8, 128256, 1) > 0          # normalize layout
+    for bad in ((0, 1, 8, 100, 1), (4, 1, 33, 100, 1), (4, 3, 22, 100, 1), (4, 1, 8, 0, 1),
+                (4, 1, 8, 100, 7), (4, 1, 8, 2 ** 31, 1)):
+        assert lib.specverify_workspace_size(*bad) == 0, bad
+
+
+def _step(lib, **over):
+    a = dict(t=8, d=8, dtype=1, tok=8, B=2, K=1, g=4, V=1000, tsb=5000, tsj=1000, dsb=4000, dsk=4000,
+             dsj=1000, T=8, seed=1, pos0=None, n=8, y=8, lp=None, lq=None, zt=None, zd=None,
+             err=None, ws=256, wsb=1 << 20, st=None)
+    a.update(over)
+    order = ["t", "d", "dtype", "tok", "B", "K", "g", "V", "tsb", "tsj", "dsb", "dsk", "dsj", "T",
+             "seed", "pos0", "n", "y", "lp", "lq", "zt", "zd", "err", "ws", "wsb", "st"]
+    return lib.specverify_step(*[a[k] for k in order])
+
+
+def test_step_argument_validation_happens_on_the_host():
+    # Fake device pointers: every call below must be rejected before any HIP call.
+    lib = sv.load_library()
+    assert _step(lib, t=None) == -1
+    assert _step(lib, tok=None) == -1
+    assert _step(lib, n=None) == -1
+    assert _step(lib, B=0) == -1
+    assert _step(lib, g=0) == -1
+    assert _step(lib, g=33) == -1
+    assert _step(lib, K=3, g=22) == -1            # K * gamma > 64
+    assert _step(lib, V=0) == -1
+    assert _step(lib, V=2 ** 31) == -1
+    assert _step(lib, tsb=-1) == -1
+    assert _step(lib, dtype=5) == -2
+    assert _step(lib, ws=None) == -3
+    need = lib.specverify_workspace_size(2, 1, 4, 1000, 1)
+    assert _step(lib, wsb=need - 1) == -3
+    assert _step(lib, ws=264) == -4                # misaligned workspace
+
+
+def test_other_entry_points_validate_on_the_host():
+    lib = sv.load_library()
+    assert lib.specverify_normalize(None, 1, 2, 3, 100, 300, 100, 8, 8, None, 256, 1 << 20, None) == -1
+    assert lib.specverify_normalize(8, 9, 2, 3, 100, 300, 100, 8, 8, None, 256, 1 << 20, None) == -2
+    assert lib.specverify_normalize(8, 1, 2, 3, 100, 300, 100, 8, 8, None, 256, 16, None) == -3
+    assert lib.specverify_accept(None, 8, 2, 1, 4, 0, None, 8, None, None) == -1
+    assert lib.specverify_accept(8, 8, 2, 1, 33, 0, None, 8, None, None) == -1
+    assert lib.specverify_accept(8, 8, 0, 1, 4, 0, None, 8, None, None) == -1
+    args = [8, 8, 1, 2, 1, 4, 1000, 5000, 1000, 4000, 4000, 1000, 8, 8, 8, 8, 8, 1, None, 8, 256,
+            1 << 20, None]
+    bad = list(args)
+    bad[15] = None                                  # accept_len
+    assert lib.specverify_residual_sample(*bad) == -1
+    bad = list(args)
+    bad[2] = 3
+    assert lib.specverify_residual_sample(*bad) == -2
+    bad = list(args)
+    bad[20] = None
+    assert lib.specverify_residual_sample(*bad) == -3
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(sv.SpecVerifyError):
+        sv.specverify_normalize(torch.zeros(1, 2, 8), torch.ones(1))

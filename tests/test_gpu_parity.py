@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: accept lengths and emitted tokens bit-exact except chains the oracle flags
+as within 1e-6 of a decision threshold; ln p / ln q within 1e-4 absolute;
+normalisers within 1e-5 relative (|d ln Z| <= 1e-5); greedy rows exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import device_draft_verification_specverify_amd as sv
+import oracle
+import workloads
+from gpu_helpers import compare_step, device, logits_to_dev, step_on_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _ref(w, rows=None):
+    if rows is None:
+        return oracle.verify(w.target, w.draft, w.tokens, w.temperature, w.seed, w.pos0,
+                             dtype=w.dtype)
+    rows = np.asarray(rows)
+    return oracle.verify(w.target[rows], w.draft[rows], w.tokens[rows], w.temperature[rows],
+                         w.seed, w.pos0[rows], batch_index=rows, dtype=w.dtype)
+
+
+def _report(name, stats):
+    print(f"[parity] {name}: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("c1", {}), ("c2", {}), ("c3", dict(B=16)), ("c4", dict(B=32)), ("c5", dict(B=4)),
+])
+def test_step_matches_oracle_reduced_batches(name, kw):
+    w = workloads.make(name, **kw)
+    print(f"[case] {name} {kw}", flush=True)
+    gpu = step_on_gpu(w)
+    _report(name, compare_step(gpu, _ref(w), w.temperature))
+    assert int(gpu["device_error"][0]) == 0
+
+
+def test_step_matches_oracle_c3_full():
+    w = workloads.make("c3")
+    print("[case] c3 full B=64", flush=True)
+    gpu = step_on_gpu(w)
+    _report("c3", compare_step(gpu, _ref(w), w.temperature))
+
+
+def test_step_matches_oracle_c4_full_sampled_rows():
+    w = workloads.make("c4")
+    print("[case] c4 full B=256, oracle on 40 rows", flush=True)
+    gpu = step_on_gpu(w)
+    rows = np.concatenate([np.arange(16), np.random.default_rng(4).choice(np.arange(16, 256), 24,
+                                                                          replace=False)])
+    _report("c4", compare_step(gpu, _ref(w, rows), w.temperature, rows))
+
+
+def test_step_matches_oracle_c5_full_sampled_rows():
+    w = workloads.make("c5")
+    print("[case] c5 full B=512 K=4, oracle on 10 rows", flush=True)
+    gpu = step_on_gpu(w)
+    rows = np.array([0, 1, 77, 128, 255, 256, 300, 411, 510, 511])
+    _report("c5", compare_step(gpu, _ref(w, rows), w.temperature, rows))
+    # properties at every chain: lengths in range, corrections differ from the rejected draft
+    n, y = gpu["accept_len"], gpu["out_token"]
+    assert np.all((n >= 0) & (n <= w.gamma)) and np.all((y >= 0) & (y < w.V))
+    bb, kk = np.nonzero(n < w.gamma)
+    assert np.all(y[bb, kk] != w.tokens[bb, kk, n[bb, kk]])
+
+
+@pytest.mark.parametrize("V,gamma,K,B,dtype", [
+    (1, 2, 1, 3, "bf16"), (7, 3, 2, 5, "f32"), (8, 1, 1, 4, "bf16"), (9, 4, 1, 6, "bf16"),
+    (1000, 5, 1, 7, "f32"), (4097, 8, 1, 9, "bf16"), (8193, 2, 3, 5, "bf16"),
+    (40001, 6, 1, 3, "f32"), (33000, 32, 2, 2, "bf16"), (5000, 16, 4, 3, "bf16"),
+])
+def test_edge_shapes(V, gamma, K, B, dtype):
+    print(f"[case] edge V={V} gamma={gamma} K={K} B={B} {dtype}", flush=True)
+    w = workloads.make("c3", B=B, V=V, gamma=gamma, K=K, dtype=dtype,
+                       temps=("choice", (0.0, 0.3, 1.0, 2.5)))
+    _report(f"edge V={V}", compare_step(step_on_gpu(w), _ref(w), w.temperature))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_unaligned_rows_take_the_element_path(dtype):
+    w = workloads.make("c2", B=5, V=3001, dtype=dtype)
+    print(f"[case] unaligned {dtype}", flush=True)
+    # views whose rows start one element past a 16-byte boundary
+    tpad = np.zeros(w.target.shape[:-1] + (w.V + 1,), dtype=w.target.dtype)
+    dpad = np.zeros(w.draft.shape[:-1] + (w.V + 1,), dtype=w.draft.dtype)
+    tpad[..., 1:] = w.target
+    dpad[..., 1:] = w.draft
+    t = logits_to_dev(tpad, w.dtype)[..., 1:]
+    d = logits_to_dev(dpad, w.dtype)[..., 1:]
+    assert t.data_ptr() % 16 != 0
+    _report("unaligned", compare_step(step_on_gpu(w, target=t, draft=d), _ref(w), w.temperature))
+
+
+def test_broadcast_target_and_draft_rows():
+    w = workloads.make("c3", B=1, V=6000)
+    B = 24
+    print("[case] broadcast stride 0", flush=True)
+    tb = np.broadcast_to(w.target, (B,) + w.target.shape[1:])
+    db = np.broadcast_to(w.draft, (B,) + w.draft.shape[1:])
+    rng = np.random.default_rng(1)
+    tokens = rng.integers(0, w.V, size=(B, 1, w.gamma)).astype(np.int32)
+    temps = np.full(B, w.temperature[0], dtype=np.float32)
+    pos0 = np.arange(B, dtype=np.int64) * 3
+    w2 = workloads.Workload("bcast", B, 1, w.gamma, w.V, w.dtype, np.ascontiguousarray(tb),
+                            np.ascontiguousarray(db), tokens, temps, pos0, w.seed)
+    t = logits_to_dev(w.target, w.dtype).expand(B, -1, -1)
+    d = logits_to_dev(w.draft, w.dtype).expand(B, -1, -1, -1)
+    assert t.stride(0) == 0 and d.stride(0) == 0
+    g_b = step_on_gpu(w2, target=t, draft=d)
+    g_c = step_on_gpu(w2)
+    for k in ("accept_len", "out_token", "logp", "logq", "lnZ_target"):
+        assert np.array_equal(g_b[k], g_c[k]), k
+    _report("broadcast", compare_step(g_b, _ref(w2), temps))
+
+
+def test_reruns_are_bit_identical():
+    w = workloads.make("c3", B=12)
+    print("[case] determinism", flush=True)
+    a = step_on_gpu(w)
+    b = step_on_gpu(w)
+    for k, v in a.items():
+        if v is not None:
+            assert np.array_equal(v, b[k], equal_nan=True), k
+
+
+def test_input_errors_set_bits_and_poison_only_their_chains():
+    w = workloads.make("c3", B=8, V=2000, temps=("const", 0.7))
+    print("[case] error paths", flush=True)
+    w.tokens[1, 0, 2] = w.V               # out of range
+    w.tokens[2, 0, 0] = -5
+    w.temperature[3] = -1.0
+    w.temperature[4] = np.nan
+    if w.dtype == "bf16":
+        w.target[5, 3, :] = 0xFF80        # -inf row
+    gpu = step_on_gpu(w)
+    ref = _ref(w)
+    assert np.array_equal(gpu["accept_len"], ref["accept_len"])
+    assert int(gpu["device_error"][0]) == ref["error"] == (1 | 2 | 4)
+    for b in (1, 2, 3, 4, 5):
+        assert gpu["accept_len"][b, 0] == -1 and gpu["out_token"][b, 0] == -1
+    good = np.array([0, 6, 7])
+    compare_step({k: (v[good] if k not in ("device_error",) and v is not None else v)
+                  for k, v in gpu.items()},
+                 {k: (v[good] if isinstance(v, np.ndarray) and v.ndim >= 1 else v)
+                  for k, v in ref.items()}, w.temperature[good])
+
+
+def test_normalize_entry_point():
+    rng = np.random.default_rng(2)
+    for V, dt in ((1, "f32"), (300, "bf16"), (128256, "bf16"), (32001, "f32")):
+        print(f"[case] normalize V={V} {dt}", flush=True)
+        B, P = 5, 3
+        z = rng.normal(0, 3, size=(B, P, V)).astype(np.float32)
+        z[0, 0, : V // 2] = -np.inf
+        raw = workloads.round_to_bf16_bits(z) if dt == "bf16" else z
+        T = np.array([0.0, 0.1, 0.7, 1.0, 3.0], dtype=np.float32)
+        lnz, am = sv.specverify_normalize(logits_to_dev(raw, dt), to_dev(T), want_argmax=True)
+        torch.cuda.synchronize()
+        zz = oracle.decode_logits(raw, dt)
+        rl, ra = oracle.normalize_rows(zz, T[:, None])
+        lnz, am = lnz.cpu().numpy(), am.cpu().numpy()
+        assert np.array_equal(am, ra)
+        assert np.array_equal(lnz[0], rl[0])                       # greedy row: the raw max
+        assert np.all(np.abs(lnz[1:] - rl[1:]) <= 1e-5), np.abs(lnz[1:] - rl[1:]).max()
+
+
+def test_accept_entry_point_reproduces_the_oracle_exactly():
+    rng = np.random.default_rng(3)
+    for B, K, g in ((256, 1, 4), (7, 4, 8), (3, 2, 32), (1, 1, 1)):
+        print(f"[case] accept B={B} K={K} gamma={g}", flush=True)
+        lp = rng.normal(-2, 1, size=(B, K, g)).astype(np.float32)
+        lq = (lp + rng.normal(0, 0.7, size=lp.shape)).astype(np.float32)
+        lp[0, 0, 0] = -np.inf                                       # greedy-style reject
+        lq[-1, -1, -1] = -np.inf
+        pos0 = rng.integers(0, 1 << 40, size=B).astype(np.int64)
+        n, bits = sv.specverify_accept(to_dev(lp), to_dev(lq), 987654321, to_dev(pos0),
+                                       want_bits=True)
+        torch.cuda.synchronize()
+        rn, rbits, _ = oracle.accept_from_logprobs(lp, lq, 987654321, pos0)
+        assert np.array_equal(n.cpu().numpy(), rn)
+        assert np.array_equal(bits.cpu().numpy().view(np.uint32), rbits)
+
+
+def test_residual_entry_point_at_every_accept_length():
+    w = workloads.make("c3", B=6, V=20000, temps=("choice", (0.0, 0.4, 1.0)))
+    print("[case] residual entry point", flush=True)
+    zt = oracle.decode_logits(w.target, w.dtype)
+    zd = oracle.decode_logits(w.draft, w.dtype)
+    ref = oracle.verify(zt, zd, w.tokens, w.temperature, w.seed, w.pos0)
+    chain_rows = np.arange(w.B)[:, None]
+    for n in range(w.gamma + 1):
+        nn = np.full((w.B, 1), n, dtype=np.int64)
+        tok, flag, _ = oracle.specverify.sample_tokens(
+            zt, zd, w.temperature.astype(np.float64), ref["lnZ_target"],
+            np.nan_to_num(ref["lnZ_draft"]), ref["argmax_target"], nn, w.seed, w.pos0, chain_rows)
+        out = sv.specverify_residual_sample(
+            logits_to_dev(w.target, w.dtype), logits_to_dev(w.draft, w.dtype), to_dev(w.temperature),
+            to_dev(ref["lnZ_target"]), to_dev(np.nan_to_num(ref["lnZ_draft"])),
+            to_dev(ref["argmax_target"].astype(np.int32)), to_dev(nn.astype(np.int32)), w.seed,
+            to_dev(w.pos0))
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got[~flag], tok[~flag]), (n, got.ravel(), tok.ravel())
