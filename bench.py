@@ -149,7 +149,7 @@ def main() -> int:
         "bytes_min_per_step": bytes_min,
         "accepted_tokens_per_step": int((out.accept_len.clamp(min=0) + 1).sum().item()),
         "device_error": err,
-        "roofline": {"bound": "hbm", "kernel": "rowstats_kernel (+finalize_rows_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "stream_kernel (+finalize_rows_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                      "bytes_per_launch": kernel_bytes, "avg_launch_ms": kern_ms},

@@ -1,31 +1,37 @@
 // specverify.hip -- HIP kernels (gfx950 / CDNA4) and the C ABI of libspecverify.
 //
-// Batched speculative-sampling verification. The pieces, in the order a step
-// runs them:
-//   rowstats_kernel   streams every needed logit row once (128-bit loads),
-//                     one wavefront per (row, chunk) unit: chunk maximum, lowest
-//                     argmax and sum of exp2((z - max) * log2e / T), reduced
-//                     across the wavefront with cross-lane shuffles.
-//   accept_kernel     one workgroup per batch row: merges the chunk partials of
-//                     the row's gamma+1 target and K*gamma draft rows into
-//                     ln Z (double), gathers ln p / ln q at the draft tokens,
-//                     draws the Philox accept uniforms and finds each chain's
-//                     first rejection with one wavefront ballot.
-//   sample_kernel     per (chain, vocabulary split): a second pass over the one
-//                     row pair the chain needs (target/draft row n for the
-//                     residual, target row gamma for the bonus), Gumbel-max by
-//                     exponential race argmin_v E_v / w_v with E_v = -ln u_v
-//                     (equivalent to argmax_v ln w_v + G_v), keeping the best
-//                     two candidates; the last workgroup of a chain merges the
-//                     splits and re-scores the two candidates in float64.
-//   accept_scalar_kernel  the accept test alone from caller-supplied ln p/ln q.
+// Batched speculative-sampling verification in three launches, none of which
+// hands data between workgroups inside a kernel (a kernel boundary is the only
+// cross-XCD synchronisation, so no L2 write-back fences are needed):
 //
-// No matrix cores: nothing on this path is a dense contraction. No
-// floating-point atomics: partials are merged in a fixed order, so results are
-// bit-deterministic.
+//   stream_kernel   every needed logit row is read exactly once. The flattened
+//                   space of (row, 8-logit vector) is cut into equal contiguous
+//                   ranges, one per resident wavefront, so every wavefront
+//                   streams the same number of bytes whatever the shape. Draft
+//                   rows of greedy batch rows are left out of that space. Each
+//                   lane keeps an online (max, sum of exp2) over its vectors
+//                   with one fma + one exp per logit; each row segment ends in
+//                   one cross-lane reduction and one 16-byte partial.
+//   chain_kernel    one workgroup per (chain, vocabulary split). It merges the
+//                   partials of its chain's rows into ln Z, gathers ln p / ln q
+//                   at the draft tokens, draws the accept uniforms and finds the
+//                   first rejection with one wavefront ballot (every split of a
+//                   chain computes the same n). Then it scans its split of the
+//                   one row pair the chain needs -- target/draft row n for the
+//                   residual, target row gamma for the bonus -- drawing Gumbel
+//                   noise by exponential race, argmin_v E_v / w_v with
+//                   E_v = -ln u_v (the same argmax as ln w_v + G_v), and keeps
+//                   its best two candidates.
+//                   The split re-scores those two in float64.
+//   finish_kernel   one wavefront per chain keeps the best float64 score over
+//                   the splits (ties to the lowest id).
+//
+// No matrix cores (nothing here is a dense contraction) and no floating-point
+// atomics: results are bit-deterministic.
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstddef>
@@ -38,11 +44,13 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kGroup = 8;                                    // consecutive vocabulary ids per lane group
-constexpr int kRowGroups = 8;                                // groups per lane per normaliser unit
-constexpr int64_t kUnit = int64_t(kWave) * kGroup * kRowGroups;  // 4096 logits per wavefront unit
-constexpr int kSampleIters = 4;                              // groups per thread per sampling split
-constexpr int64_t kSplit = int64_t(kBlock) * kGroup * kSampleIters;  // 8192 ids per workgroup
+constexpr int kVec = 8;                    // logits per vector (16 B of bf16, 32 B of f32)
+constexpr int kUnroll = 4;                 // vectors in flight per lane in the stream loop
+constexpr int kSampleIters = 4;            // vectors per thread per sampling split
+constexpr int64_t kSplit = int64_t(kBlock) * kVec * kSampleIters;  // 8192 ids per split
+constexpr int64_t kMaxWaves = 16384;       // cap on stream wavefronts (sizes the workspace)
+constexpr int64_t kMaxCompactB = 16384;    // batch rows whose greedy drafts are compacted out
+constexpr int kMaxRowsPerChain = SV_MAX_GAMMA + 1 + SV_MAX_GAMMA;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr double kLog2eD = 1.44269504088896340736;
 constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
@@ -52,11 +60,12 @@ constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
 constexpr uint32_t kPurposeAccept = 0;
 constexpr uint32_t kPurposeSample = 1;
 
-// Statistics of one (row, chunk) unit.
+// Statistics of one row segment: s = sum over the segment of 2^((z - m) * k),
+// k = float(log2(e) / T); m is the raw maximum and idx its lowest id.
 struct alignas(16) RowPartial {
-  float m;      // largest raw logit in the chunk (-inf if none)
-  int32_t idx;  // lowest id holding it (INT_MAX if none)
-  double s;     // sum of exp2((z - m) * log2e / T) over the chunk (sampled rows)
+  float m;
+  int32_t idx;
+  double s;
 };
 
 // Best two sampling candidates of one split, ordered by (key, id).
@@ -65,6 +74,21 @@ struct alignas(16) Top2 {
   int32_t i1;
   float k2;
   int32_t i2;
+};
+
+// A split's draw result: the float64 score ln w_v + G_v of its best candidate.
+struct alignas(16) Cand {
+  double score;  // -inf when the split holds no candidate
+  int32_t id;    // INT_MAX when none
+  int32_t pad;
+};
+
+// What the finish kernel needs of a chain (written by split 0 of the chain kernel).
+struct alignas(16) ChainInfo {
+  double lzt;  // ln Z of the target row the token is drawn from (row n, or gamma)
+  double lzd;  // ln Z of draft row n (residual draws)
+  int32_t n;   // accept length; -1 when no draw is needed (greedy, error)
+  int32_t pad[3];
 };
 
 // ---------------------------------------------------------------------------
@@ -106,7 +130,7 @@ __device__ __forceinline__ double log_uniform_d(double u) {
 }
 
 // ---------------------------------------------------------------------------
-// Loading 8 consecutive logits (ids e0 .. e0+7) as float; ids >= end read -inf.
+// Logit access. A "vector" is 8 consecutive logits starting at a multiple of 8.
 template <int DT>
 __device__ __forceinline__ float load_one(const void* row, int64_t e) {
   if constexpr (DT == SV_BF16) {
@@ -117,66 +141,89 @@ __device__ __forceinline__ float load_one(const void* row, int64_t e) {
   }
 }
 
-template <int DT, bool VEC>
-__device__ __forceinline__ void load8(const void* row, int64_t e0, int64_t end, float (&x)[kGroup]) {
-  if (VEC && e0 + kGroup <= end) {
-    if constexpr (DT == SV_BF16) {
-      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(row) + e0);
-      x[0] = __uint_as_float(w.x << 16);
-      x[1] = __uint_as_float(w.x & 0xFFFF0000u);
-      x[2] = __uint_as_float(w.y << 16);
-      x[3] = __uint_as_float(w.y & 0xFFFF0000u);
-      x[4] = __uint_as_float(w.z << 16);
-      x[5] = __uint_as_float(w.z & 0xFFFF0000u);
-      x[6] = __uint_as_float(w.w << 16);
-      x[7] = __uint_as_float(w.w & 0xFFFF0000u);
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(row) + e0);
-      const float4 a = p[0];
-      const float4 b = p[1];
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+// Raw storage of one vector: 4 dwords of bf16 pairs, or 8 floats.
+template <int DT>
+struct RawVec {
+  uint32_t w[DT == SV_BF16 ? 4 : 8];
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// All 8 ids of vector vi must lie inside the row. NT: non-temporal 128-bit loads
+// (logits are read once; streaming them past the caches measured ~8% faster).
+template <int DT, bool VEC, bool NT = false>
+__device__ __forceinline__ RawVec<DT> load_vec(const void* row, int64_t vi) {
+  RawVec<DT> r;
+  if constexpr (VEC) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row) + (DT == SV_BF16 ? vi : 2 * vi);
+    const u32x4 a = NT ? __builtin_nontemporal_load(p) : p[0];
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    if constexpr (DT == SV_F32) {
+      const u32x4 b = NT ? __builtin_nontemporal_load(p + 1) : p[1];
+      r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
     }
   } else {
+    if constexpr (DT == SV_BF16) {
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(row) + kVec * vi;
 #pragma unroll
-    for (int t = 0; t < kGroup; ++t) x[t] = (e0 + t < end) ? load_one<DT>(row, e0 + t) : -INFINITY;
+      for (int i = 0; i < 4; ++i) r.w[i] = uint32_t(p[2 * i]) | (uint32_t(p[2 * i + 1]) << 16);
+    } else {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(row) + kVec * vi;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r.w[i] = p[i];
+    }
   }
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ float vec_elem(const RawVec<DT>& r, int t) {
+  if constexpr (DT == SV_BF16) {
+    const uint32_t w = r.w[t >> 1];
+    return __uint_as_float((t & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  } else {
+    return __uint_as_float(r.w[t]);
+  }
+}
+
+// A vector that reads -inf in every slot.
+template <int DT>
+__device__ __forceinline__ RawVec<DT> neg_inf_vec() {
+  RawVec<DT> r;
+  if constexpr (DT == SV_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = 0xFF80FF80u;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.w[i] = 0xFF800000u;
+  }
+  return r;
+}
+
+// Vector vi of a row of V logits, ids >= V reading -inf (only a row's last
+// vector can be partial; it is read element by element).
+template <int DT, bool VEC>
+__device__ __forceinline__ RawVec<DT> load_vec_bounded(const void* row, int64_t vi, int64_t V) {
+  if ((vi + 1) * kVec <= V) return load_vec<DT, VEC>(row, vi);
+  RawVec<DT> r = neg_inf_vec<DT>();
+#pragma unroll
+  for (int t = 0; t < kVec; ++t) {
+    const int64_t e = vi * kVec + t;
+    if (e < V) {
+      if constexpr (DT == SV_BF16) {
+        const uint32_t h = reinterpret_cast<const uint16_t*>(row)[e];
+        r.w[t >> 1] = (t & 1) ? ((r.w[t >> 1] & 0x0000FFFFu) | (h << 16))
+                              : ((r.w[t >> 1] & 0xFFFF0000u) | h);
+      } else {
+        r.w[t] = reinterpret_cast<const uint32_t*>(row)[e];
+      }
+    }
+  }
+  return r;
 }
 
 __device__ __forceinline__ const void* row_ptr(const void* base, int esz, int64_t off_elems) {
   return reinterpret_cast<const char*>(base) + off_elems * esz;
-}
-
-// ---------------------------------------------------------------------------
-// Rows to normalise. Target rows: rho in [0, B*P): b = rho / P, j = rho % P.
-// Draft rows: rho in [B*P, B*P + B*K*G): the rest in [b][k][j] order.
-struct RowSet {
-  const void* t;
-  int64_t tsb, tsj;
-  const void* d;
-  int64_t dsb, dsk, dsj;
-  int64_t B, P, K, G;
-  const float* temp;
-};
-
-__device__ __forceinline__ void locate_row(const RowSet& rs, int64_t rho, int esz, const void*& ptr,
-                                           int64_t& b, bool& is_draft) {
-  const int64_t nt = rs.B * rs.P;
-  if (rho < nt) {
-    b = rho / rs.P;
-    const int64_t j = rho - b * rs.P;
-    ptr = row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj);
-    is_draft = false;
-  } else {
-    const int64_t r = rho - nt;
-    const int64_t kg = rs.K * rs.G;
-    b = r / kg;
-    const int64_t rem = r - b * kg;
-    const int64_t k = rem / rs.G;
-    const int64_t j = rem - k * rs.G;
-    ptr = row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj);
-    is_draft = true;
-  }
 }
 
 __device__ __forceinline__ void better_max(float& m, int32_t& i, float om, int32_t oi) {
@@ -186,282 +233,433 @@ __device__ __forceinline__ void better_max(float& m, int32_t& i, float om, int32
   }
 }
 
-// One wavefront per (row, chunk) unit, grid-stride over units.
-template <int DT, bool VEC, bool ARGMAX_ALL>
-__global__ __launch_bounds__(kBlock) void rowstats_kernel(RowSet rs, int64_t V, int64_t nch,
-                                                          int64_t clen, int64_t nunits,
-                                                          RowPartial* __restrict__ part) {
-  constexpr int esz = DT == SV_BF16 ? 2 : 4;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t nwaves = int64_t(gridDim.x) * kWavesPerBlock;
-  for (int64_t u = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6); u < nunits;
-       u += nwaves) {
-    const int64_t rho = u / nch;
-    const int64_t c = u - rho * nch;
-    const void* row;
-    int64_t b;
-    bool is_draft;
-    locate_row(rs, rho, esz, row, b, is_draft);
-    const float T = rs.temp[b];
-    const bool sampled = T > 0.0f;
-    if (is_draft && !sampled) continue;  // greedy chains never read their draft rows
-    const int64_t start = c * clen;
-    const int64_t end = start + clen < V ? start + clen : V;
+// ---------------------------------------------------------------------------
+// Rows and their place in the flattened stream. Target rows come first, in
+// (b, j) order; then the K*G draft rows of every batch row that needs them, in
+// (b, k, j) order. In compact mode only batch rows with T > 0 contribute draft
+// rows; otherwise all do and greedy ones are skipped in place.
+struct RowSet {
+  const void* t;
+  int64_t tsb, tsj;
+  const void* d;
+  int64_t dsb, dsk, dsj;
+  int64_t B, P, K, G;
+  const float* temp;
+};
 
-    float x[kRowGroups][kGroup];
-#pragma unroll
-    for (int g = 0; g < kRowGroups; ++g) {
-      const int64_t e0 = start + int64_t(kGroup) * (lane + kWave * g);
-      if (e0 < end) {
-        load8<DT, VEC>(row, e0, end, x[g]);
-      } else {
-#pragma unroll
-        for (int t = 0; t < kGroup; ++t) x[g][t] = -INFINITY;
-      }
-    }
+struct Partition {
+  int64_t vpr;     // vectors per row
+  int64_t nrows;   // rows in the flattened space
+  int64_t N;       // vectors in the flattened space
+  int64_t W;       // stream wavefronts
+  int64_t maxseg;  // partial slots per wavefront
+};
 
-    float m = -INFINITY;
-    int32_t idx = INT_MAX;
-    if (!sampled || ARGMAX_ALL) {
-#pragma unroll
-      for (int g = 0; g < kRowGroups; ++g) {
-        const int64_t e0 = start + int64_t(kGroup) * (lane + kWave * g);
-#pragma unroll
-        for (int t = 0; t < kGroup; ++t) {
-          if (x[g][t] > m) {
-            m = x[g][t];
-            idx = int32_t(e0 + t);
-          }
-        }
-      }
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        const float om = __shfl_xor(m, off, kWave);
-        const int32_t oi = __shfl_xor(idx, off, kWave);
-        better_max(m, idx, om, oi);
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < kRowGroups; ++g)
-#pragma unroll
-        for (int t = 0; t < kGroup; ++t) m = fmaxf(m, x[g][t]);
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    }
-
-    double s = 0.0;
-    if (sampled) {
-      const float k2 = kLog2e / T;
-      const float m0 = (m == -INFINITY) ? 0.0f : m;
-#pragma unroll
-      for (int g = 0; g < kRowGroups; ++g) {
-        float sg = 0.0f;
-#pragma unroll
-        for (int t = 0; t < kGroup; ++t) sg += __builtin_amdgcn_exp2f((x[g][t] - m0) * k2);
-        s += double(sg);
-      }
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
-    }
-    if (lane == 0) part[u] = RowPartial{m, idx, s};
-  }
+__device__ __forceinline__ int64_t range_lo(const Partition& p, int64_t w) {
+  return (w * p.N) / p.W;
+}
+// The wavefront whose range holds flattened vector `pos`.
+__device__ __forceinline__ int64_t wave_of(const Partition& p, int64_t pos) {
+  return ((pos + 1) * p.W - 1) / p.N;
 }
 
-// Merge the chunk partials of one row in chunk order: (max, lowest argmax, ln Z).
+// Merge the stream partials of flattened row rho in wavefront order. Waves
+// w0..w1 hold the row's first and last vector; when the stream has fewer
+// vectors than wavefronts some waves in between have empty ranges and wrote
+// nothing, so they are skipped.
 struct RowStat {
   double lnz;
   float m;
   int32_t idx;
 };
 
-__device__ RowStat merge_row(const RowPartial* __restrict__ p, int64_t nch, float T) {
+template <int NB = 8>
+__device__ RowStat merge_row(const RowPartial* __restrict__ part, const Partition& p, int64_t rho,
+                             float T) {
+  const int64_t first = rho * p.vpr;
+  const int64_t w0 = wave_of(p, first);
+  const int64_t w1 = wave_of(p, first + p.vpr - 1);
   float m = -INFINITY;
   int32_t idx = INT_MAX;
-  for (int64_t c = 0; c < nch; ++c) better_max(m, idx, p[c].m, p[c].idx);
+  double s = 0.0;
+  const double k2 = double(kLog2e / T);
+  // Partials are fetched NB at a time so their latencies overlap; each batch is
+  // folded into (m, s) with s rescaled when the maximum grows (exponents exact
+  // in double). The fold order is fixed, so the result is deterministic.
+  for (int64_t w = w0; w <= w1; w += NB) {
+    RowPartial buf[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t ww = w + i;
+      const int64_t lo = range_lo(p, ww);
+      buf[i] = RowPartial{-INFINITY, INT_MAX, 0.0};
+      if (ww <= w1 && lo < range_lo(p, ww + 1)) buf[i] = part[ww * p.maxseg + (rho - lo / p.vpr)];
+    }
+    float bm = m;
+    int32_t bi = idx;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) better_max(bm, bi, buf[i].m, buf[i].idx);
+    if (T > 0.0f && bm > -INFINITY) {
+      if (m > -INFINITY) s *= exp2((double(m) - double(bm)) * k2);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (buf[i].m != -INFINITY) s += buf[i].s * exp2((double(buf[i].m) - double(bm)) * k2);
+    }
+    m = bm;
+    idx = bi;
+  }
   RowStat r;
   r.m = m;
   r.idx = idx;
-  if (T > 0.0f) {
-    if (!(m > -INFINITY)) {
-      r.lnz = double(m);  // -inf (all masked) or NaN
-    } else {
-      const double k2 = kLog2eD / double(T);
-      double s = 0.0;
-      for (int64_t c = 0; c < nch; ++c) {
-        if (p[c].m == -INFINITY) continue;
-        s += p[c].s * exp2(double(p[c].m - m) * k2);
-      }
-      r.lnz = double(m) / double(T) + log(s);
-    }
-  } else if (T == 0.0f) {
-    r.lnz = double(m);
-  } else {
-    r.lnz = NAN;
-  }
+  if (T > 0.0f) r.lnz = (m > -INFINITY) ? double(m) / double(T) + log(s) : double(m);
+  else if (T == 0.0f) r.lnz = double(m);
+  else r.lnz = NAN;
   return r;
 }
 
-// ln Z and argmax of every row (specverify_normalize).
+// ---------------------------------------------------------------------------
+// Which batch rows need draft rows: a ballot mask per 64 batch rows and an
+// exclusive prefix of their counts, built in LDS by every stream workgroup.
+struct SampledTable {
+  uint64_t mask[kMaxCompactB / 64];
+  int32_t pref[kMaxCompactB / 64 + 1];
+  int32_t wsum[kWavesPerBlock];
+};
+
+__device__ void build_sampled_table(const float* __restrict__ temp, int64_t B, SampledTable& tab) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int nchunks = int((B + 63) / 64);
+  for (int c = wid; c < nchunks; c += kWavesPerBlock) {
+    const int64_t b = int64_t(c) * 64 + lane;
+    const bool s = b < B && temp[b] > 0.0f;
+    const uint64_t m = __ballot(s);
+    if (lane == 0) tab.mask[c] = m;
+  }
+  __syncthreads();
+  // inclusive scan of per-chunk counts, one chunk per thread (nchunks <= 256)
+  int x = int(threadIdx.x) < nchunks ? __popcll(tab.mask[threadIdx.x]) : 0;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) tab.wsum[wid] = x;
+  __syncthreads();
+  for (int w = 0; w < wid; ++w) x += tab.wsum[w];
+  if (int(threadIdx.x) < nchunks) tab.pref[threadIdx.x + 1] = x;
+  if (threadIdx.x == 0) tab.pref[0] = 0;
+  __syncthreads();
+}
+
+// Batch row of the s-th sampled batch row (0-based).
+__device__ int64_t select_sampled(const SampledTable& tab, int nchunks, int64_t s) {
+  int lo = 0, hi = nchunks - 1;
+  while (lo < hi) {  // last chunk c with pref[c] <= s
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab.pref[mid] <= s) lo = mid;
+    else hi = mid - 1;
+  }
+  uint64_t m = tab.mask[lo];
+  for (int64_t r = s - tab.pref[lo]; r > 0; --r) m &= m - 1;
+  return int64_t(lo) * 64 + __builtin_ctzll(m);
+}
+
+struct StreamArgs {
+  RowSet rs;
+  int64_t V;
+  Partition p;           // in compact mode nrows and N are recomputed on the device
+  int compact;
+  RowPartial* part;      // [W][maxseg]
+  int32_t* rank_out;     // [B + 1]: sampled batch rows before b; [B] = their total
+};
+
+// Online statistics of one lane over the vectors it reads in one row segment.
+// Sampled rows: running raw maximum m, c = float(m * k2) and s = sum of
+// 2^(z*k2 - c) (one fma + one exp per logit); greedy rows: maximum and lowest
+// argmax only. ARGMAX also tracks the argmax of sampled rows.
+template <int DT, bool SAMPLED, bool ARGMAX>
+struct LaneStats {
+  float m = -INFINITY;
+  float c = 0.0f;
+  double s = 0.0;
+  float am = -INFINITY;
+  int32_t idx = INT_MAX;
+  float k2 = 0.0f;
+
+  __device__ __forceinline__ void add(const RawVec<DT>* r, int n, int64_t vi0, int64_t vstride) {
+    if constexpr (SAMPLED) {
+      float lm = -INFINITY;
+      for (int u = 0; u < n; ++u)
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) lm = fmaxf(lm, vec_elem<DT>(r[u], t));
+      if constexpr (ARGMAX) track(r, n, vi0, vstride);
+      if (lm > m) {
+        // s is 0 while m = -inf; scaling it there could compute 0 * inf
+        const float cn = lm * k2;
+        if (m != -INFINITY) s *= double(__builtin_amdgcn_exp2f(c - cn));
+        c = cn;
+        m = lm;
+      }
+      float acc = 0.0f;
+      for (int u = 0; u < n; ++u) {
+        float sv = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) sv += __builtin_amdgcn_exp2f(fmaf(vec_elem<DT>(r[u], t), k2, -c));
+        acc += sv;
+      }
+      s += double(acc);
+    } else {
+      track(r, n, vi0, vstride);
+    }
+  }
+
+  __device__ __forceinline__ void track(const RawVec<DT>* r, int n, int64_t vi0, int64_t vstride) {
+    for (int u = 0; u < n; ++u)
+#pragma unroll
+      for (int t = 0; t < kVec; ++t) {
+        const float x = vec_elem<DT>(r[u], t);
+        if (x > am) {
+          am = x;
+          idx = int32_t((vi0 + vstride * u) * kVec + t);
+        }
+      }
+  }
+};
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_group(const void* row, int64_t vi0, RawVec<DT> (&r)[kUnroll]) {
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) r[u] = load_vec<DT, VEC, true>(row, vi0 + int64_t(kWave) * u);
+}
+
+// Vectors [v0, v1) of one row: lane l reads v0 + l + 64*i. Full groups of
+// 64*kUnroll vectors run without bounds checks, the next group's loads issued
+// before the current group is reduced; the last partial group is masked.
+template <int DT, bool VEC, bool SAMPLED, bool ARGMAX>
+__device__ __forceinline__ void scan_segment(const void* row, int64_t v0, int64_t v1, int lane,
+                                             LaneStats<DT, SAMPLED, ARGMAX>& st) {
+  constexpr int64_t step = int64_t(kWave) * kUnroll;
+  const int64_t nfull = (v1 - v0) / step;
+  int64_t base = v0;
+  if (nfull > 0) {
+    RawVec<DT> ra[kUnroll], rb[kUnroll];
+    load_group<DT, VEC>(row, base + lane, ra);
+    int64_t it = 0;
+    for (; it + 2 <= nfull; it += 2) {
+      load_group<DT, VEC>(row, base + step + lane, rb);
+      st.add(ra, kUnroll, base + lane, kWave);
+      if (it + 2 < nfull) load_group<DT, VEC>(row, base + 2 * step + lane, ra);
+      st.add(rb, kUnroll, base + step + lane, kWave);
+      base += 2 * step;
+    }
+    if (it < nfull) {
+      st.add(ra, kUnroll, base + lane, kWave);
+      base += step;
+    }
+  }
+  if (base < v1) {
+    RawVec<DT> r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t vi = base + lane + int64_t(kWave) * u;
+      r[u] = vi < v1 ? load_vec<DT, VEC, true>(row, vi) : neg_inf_vec<DT>();
+    }
+    st.add(r, kUnroll, base + lane, kWave);
+  }
+}
+
+// Finish one row segment: lane 0 adds the row's partial last vector if the
+// segment holds it, then the wavefront reduces to one partial (fixed order).
+template <int DT, bool VEC, bool SAMPLED, bool ARGMAX>
+__device__ __forceinline__ RowPartial finish_segment(const void* row, bool tail, int64_t vtail,
+                                                     int64_t V, int lane,
+                                                     LaneStats<DT, SAMPLED, ARGMAX>& st) {
+  if (tail && lane == 0) {
+    const RawVec<DT> rv = load_vec_bounded<DT, VEC>(row, vtail, V);
+    st.add(&rv, 1, vtail, 0);
+  }
+  if constexpr (SAMPLED) {
+    // s = sum 2^(z*k2 - c); bring every lane to the wavefront maximum M:
+    // 2^((z - M) * k2) = 2^(z*k2 - c) * 2^(c - M*k2), exponent exact in double.
+    float M = st.m;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+    double s = st.m != -INFINITY ? st.s * exp2(double(st.c) - double(M) * double(st.k2)) : 0.0;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+    int32_t idx = st.idx;
+    if constexpr (ARGMAX) {
+      float am = st.am;
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        const float om = __shfl_xor(am, off, kWave);
+        const int32_t oi = __shfl_xor(idx, off, kWave);
+        better_max(am, idx, om, oi);
+      }
+    }
+    return RowPartial{M, idx, s};
+  } else {
+    float am = st.am;
+    int32_t idx = st.idx;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const float om = __shfl_xor(am, off, kWave);
+      const int32_t oi = __shfl_xor(idx, off, kWave);
+      better_max(am, idx, om, oi);
+    }
+    return RowPartial{am, idx, 0.0};
+  }
+}
+
+// One wavefront's contiguous range of the flattened stream.
+template <int DT, bool VEC, bool ARGMAX_ALL>
+__global__ __launch_bounds__(kBlock) void stream_kernel(StreamArgs a) {
+  __shared__ SampledTable tab;
+  constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  const RowSet& rs = a.rs;
+  const int lane = threadIdx.x & (kWave - 1);
+  Partition p = a.p;
+  const int64_t BP = rs.B * rs.P;
+  const int64_t KG = rs.K * rs.G;
+  const int nchunks = int((rs.B + 63) / 64);
+  if (a.compact) {
+    build_sampled_table(rs.temp, rs.B, tab);
+    p.nrows = BP + int64_t(tab.pref[nchunks]) * KG;
+    p.N = p.nrows * p.vpr;
+    if (blockIdx.x == 0 && a.rank_out) {
+      for (int64_t b = threadIdx.x; b < rs.B; b += kBlock) {
+        const int c = int(b >> 6);
+        a.rank_out[b] = tab.pref[c] + __popcll(tab.mask[c] & ((1ull << (b & 63)) - 1ull));
+      }
+      if (threadIdx.x == 0) a.rank_out[rs.B] = tab.pref[nchunks];
+    }
+  }
+  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  if (w >= p.W) return;
+  const int64_t hi = range_lo(p, w + 1);
+  int64_t pos = range_lo(p, w);
+  int seg = 0;
+  const bool v_tail = (a.V % kVec) != 0;
+  while (pos < hi) {
+    const int64_t rho = pos / p.vpr;
+    const int64_t rstart = rho * p.vpr;
+    const int64_t seg_end = hi < rstart + p.vpr ? hi : rstart + p.vpr;
+    // locate the row
+    const void* row;
+    int64_t b;
+    bool is_draft;
+    if (rho < BP) {
+      b = rho / rs.P;
+      const int64_t j = rho - b * rs.P;
+      row = row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj);
+      is_draft = false;
+    } else {
+      const int64_t d = rho - BP;
+      const int64_t sidx = d / KG;
+      b = a.compact ? select_sampled(tab, nchunks, sidx) : sidx;
+      const int64_t rem = d - sidx * KG;
+      const int64_t k = rem / rs.G;
+      const int64_t j = rem - k * rs.G;
+      row = row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj);
+      is_draft = true;
+    }
+    const float T = rs.temp[b];
+    const bool sampled = T > 0.0f;
+    RowPartial out{-INFINITY, INT_MAX, 0.0};
+    if (!(is_draft && !sampled)) {
+      const int64_t v0 = pos - rstart;
+      int64_t v1 = seg_end - rstart;
+      // the partial last vector of a row (V % 8 != 0) is added by lane 0 at the end
+      const bool tail = v_tail && v1 == p.vpr;
+      if (tail) v1 -= 1;
+      if (sampled) {
+        LaneStats<DT, true, ARGMAX_ALL> st;
+        st.k2 = kLog2e / T;
+        scan_segment<DT, VEC>(row, v0, v1, lane, st);
+        out = finish_segment<DT, VEC>(row, tail, p.vpr - 1, a.V, lane, st);
+      } else {
+        // greedy row (or invalid temperature): maximum and lowest argmax only
+        LaneStats<DT, false, true> st;
+        scan_segment<DT, VEC>(row, v0, v1, lane, st);
+        out = finish_segment<DT, VEC>(row, tail, p.vpr - 1, a.V, lane, st);
+      }
+    }
+    if (lane == 0) a.part[w * p.maxseg + seg] = out;
+    ++seg;
+    pos = seg_end;
+  }
+}
+
+// ln Z and argmax of every row (specverify_normalize): one wavefront per row,
+// lane i folding the row's partials i, i+64, ... so their loads overlap.
 __global__ __launch_bounds__(kBlock) void finalize_rows_kernel(const RowPartial* __restrict__ part,
-                                                               int64_t nrows, int64_t P, int64_t nch,
+                                                               Partition p, int64_t P,
                                                                const float* __restrict__ temp,
                                                                double* __restrict__ lnz,
                                                                int32_t* __restrict__ amax) {
-  const int64_t rho = int64_t(blockIdx.x) * kBlock + threadIdx.x;
-  if (rho >= nrows) return;
-  const RowStat r = merge_row(part + rho * nch, nch, temp[rho / P]);
-  lnz[rho] = r.lnz;
-  if (amax) amax[rho] = r.idx == INT_MAX ? 0 : r.idx;
-}
-
-// ---------------------------------------------------------------------------
-struct AcceptArgs {
-  RowSet rs;
-  int64_t V, nch;
-  const RowPartial* part;
-  const int32_t* tokens;
-  uint64_t seed;
-  const int64_t* pos0;
-  int32_t* accept_len;
-  int32_t* out_token;
-  float* logp;
-  float* logq;
-  double* lnz_t_out;
-  double* lnz_d_out;
-  int32_t* dev_err;
-  double* ws_lnz;    // [B*P + B*K*G] normalisers of every row
-  uint32_t* ws_cnt;  // [B*K] sampling counters, zeroed here
-};
-
-// One workgroup per batch row: normalisers, gathers, accept tests, first rejections.
-template <int DT>
-__global__ __launch_bounds__(kBlock) void accept_kernel(AcceptArgs a) {
-  constexpr int esz = DT == SV_BF16 ? 2 : 4;
-  __shared__ double s_lnz[SV_MAX_GAMMA + 1 + SV_MAX_CHAIN_DECISIONS];
-  __shared__ int32_t s_amax[SV_MAX_GAMMA + 1];
-  __shared__ int32_t s_bad[SV_MAX_GAMMA + 1 + SV_MAX_CHAIN_DECISIONS];
-  const RowSet& rs = a.rs;
-  const int64_t b = blockIdx.x;
-  const int P = int(rs.P);
-  const int G = int(rs.G);
-  const int K = int(rs.K);
-  const int KG = K * G;
-  const int t = threadIdx.x;
-  const float T = rs.temp[b];
-  const bool sampled = T > 0.0f;
-  const bool greedy = T == 0.0f;
-
-  if (t < P + KG) {
-    const bool is_draft = t >= P;
-    const int64_t rho = is_draft ? rs.B * P + b * KG + (t - P) : b * P + t;
-    double lnz = NAN;
-    int32_t bad = 0;
-    if (!is_draft || sampled) {
-      const RowStat r = merge_row(a.part + rho * a.nch, a.nch, T);
-      lnz = r.lnz;
-      bad = !(r.m > -INFINITY);
-      if (!is_draft) s_amax[t] = r.idx == INT_MAX ? 0 : r.idx;
+  const int64_t rho = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  if (rho >= p.nrows) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float T = temp[rho / P];
+  const int64_t first = rho * p.vpr;
+  const int64_t w0 = wave_of(p, first);
+  const int64_t w1 = wave_of(p, first + p.vpr - 1);
+  float m = -INFINITY;
+  int32_t idx = INT_MAX;
+  double s = 0.0;
+  const double k2 = double(kLog2e / T);
+  for (int64_t ww = w0 + lane; ww <= w1; ww += kWave) {
+    const int64_t lo = range_lo(p, ww);
+    if (!(lo < range_lo(p, ww + 1))) continue;
+    const RowPartial q = part[ww * p.maxseg + (rho - lo / p.vpr)];
+    float bm = m;
+    int32_t bi = idx;
+    better_max(bm, bi, q.m, q.idx);
+    if (T > 0.0f && bm > -INFINITY) {
+      if (m > -INFINITY) s *= exp2((double(m) - double(bm)) * k2);
+      if (q.m != -INFINITY) s += q.s * exp2((double(q.m) - double(bm)) * k2);
     }
-    s_lnz[t] = lnz;
-    s_bad[t] = bad;
-    a.ws_lnz[rho] = lnz;
-    if (!is_draft && a.lnz_t_out) a.lnz_t_out[b * P + t] = lnz;
-    if (is_draft && sampled && a.lnz_d_out) a.lnz_d_out[b * KG + (t - P)] = lnz;
+    m = bm;
+    idx = bi;
   }
-  if (t < K) a.ws_cnt[b * K + t] = 0u;
-  __syncthreads();
-
-  if (t < kWave) {  // wavefront 0 decides every (branch, position) of this batch row
-    bool acc = false;
-    bool tok_bad = false;
-    if (t < KG) {
-      const int k = t / G;
-      const int j = t - k * G;
-      const int64_t chain = b * K + k;
-      const int32_t x = a.tokens[chain * G + j];
-      tok_bad = x < 0 || int64_t(x) >= a.V;
-      double lp = 0.0, lq = 0.0;
-      if (!tok_bad) {
-        if (sampled) {
-          const float zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj), x);
-          const float zd =
-              load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj), x);
-          lp = double(zt) / double(T) - s_lnz[j];
-          lq = double(zd) / double(T) - s_lnz[P + t];
-          const uint64_t pos = uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(j);
-          const Philox4 r = philox4x32_10(0u, uint32_t(pos), uint32_t(chain), kPurposeAccept,
-                                          uint32_t(a.seed), uint32_t(a.seed >> 32));
-          acc = log_uniform_d(unit_uniform_d(r.w[0])) < lp - lq;
-        } else if (greedy) {
-          acc = x == s_amax[j];
-          lp = acc ? 0.0 : -INFINITY;
-          lq = 0.0;
-        }
-      }
-      if (a.logp) a.logp[chain * G + j] = float(lp);
-      if (a.logq) a.logq[chain * G + j] = float(lq);
-    }
-    const uint64_t acc_mask = __ballot(acc);
-    const uint64_t bad_mask = __ballot(tok_bad);
-    if (t < K) {
-      const uint64_t low = (G == 64) ? ~0ull : ((1ull << G) - 1ull);
-      const uint64_t bits = (acc_mask >> (t * G)) & low;
-      const int n = __builtin_ctzll(~bits);  // leading accepts; <= G since bit G of ~bits is set
-      int32_t err = 0;
-      if ((bad_mask >> (t * G)) & low) err |= SV_ERR_TOKEN;
-      if (!(sampled || greedy)) err |= SV_ERR_TEMP;
-      for (int j = 0; j < P; ++j) err |= s_bad[j] ? SV_ERR_ROW : 0;
-      if (sampled)
-        for (int j = 0; j < G; ++j) err |= s_bad[P + t * G + j] ? SV_ERR_ROW : 0;
-      const int64_t chain = b * K + t;
-      if (err) {
-        a.accept_len[chain] = -1;
-        a.out_token[chain] = -1;
-        if (a.dev_err) atomicOr(a.dev_err, err);
-      } else {
-        a.accept_len[chain] = n;
-        if (greedy) a.out_token[chain] = s_amax[n];
-      }
-    }
+  float M = m;
+  int32_t I = idx;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const float om = __shfl_xor(M, off, kWave);
+    const int32_t oi = __shfl_xor(I, off, kWave);
+    better_max(M, I, om, oi);
+  }
+  if (T > 0.0f && M > -INFINITY) {
+    s = m > -INFINITY ? s * exp2((double(m) - double(M)) * k2) : 0.0;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+  }
+  if (lane == 0) {
+    double r;
+    if (T > 0.0f) r = M > -INFINITY ? double(M) / double(T) + log(s) : double(M);
+    else if (T == 0.0f) r = double(M);
+    else r = NAN;
+    lnz[rho] = r;
+    if (amax) amax[rho] = I == INT_MAX ? 0 : I;
   }
 }
 
 // ---------------------------------------------------------------------------
-struct SampleArgs {
-  const void* t;
-  int64_t tsb, tsj;
-  const void* d;
-  int64_t dsb, dsk, dsj;
-  int64_t B, K, G, V;
-  const float* temp;
-  const double* lnz_t;  // [B, G+1]
-  const double* lnz_d;  // [B, K, G]
-  const int32_t* amax_t;  // [B, G+1] or NULL (then greedy chains are left alone)
-  const int32_t* accept_len;
-  uint64_t seed;
-  const int64_t* pos0;
-  int32_t* out_token;
-  int64_t nsplit;
-  Top2* part;
-  uint32_t* cnt;
-};
-
 __device__ __forceinline__ bool cand_less(float ka, int32_t ia, float kb, int32_t ib) {
   return ka < kb || (ka == kb && ia < ib);
 }
 
-__device__ __forceinline__ void top2_insert(Top2& s, float key, int32_t id) {
-  if (cand_less(key, id, s.k2, s.i2)) {
-    if (cand_less(key, id, s.k1, s.i1)) {
-      s.k2 = s.k1;
-      s.i2 = s.i1;
-      s.k1 = key;
-      s.i1 = id;
-    } else {
-      s.k2 = key;
-      s.i2 = id;
-    }
-  }
+// Insert a candidate whose id is larger than every id already held (the ids a
+// thread visits only grow), so ties keep the earlier, lower id; no branches.
+__device__ __forceinline__ void top2_push(Top2& s, float key, int32_t id) {
+  const bool b1 = key < s.k1;
+  const bool b2 = key < s.k2;
+  s.k2 = b1 ? s.k1 : (b2 ? key : s.k2);
+  s.i2 = b1 ? s.i1 : (b2 ? id : s.i2);
+  s.k1 = b1 ? key : s.k1;
+  s.i1 = b1 ? id : s.i1;
 }
 
 __device__ __forceinline__ Top2 top2_merge(const Top2& a, const Top2& b) {
@@ -484,8 +682,7 @@ __device__ __forceinline__ Top2 top2_merge(const Top2& a, const Top2& b) {
 
 __device__ __forceinline__ Top2 top2_empty() { return Top2{INFINITY, INT_MAX, INFINITY, INT_MAX}; }
 
-// Workgroup-wide top-2 (every thread returns the result).
-__device__ Top2 block_top2(Top2 v, Top2* sh) {
+__device__ __forceinline__ Top2 wave_top2(Top2 v) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) {
     Top2 o;
@@ -495,39 +692,40 @@ __device__ Top2 block_top2(Top2 v, Top2* sh) {
     o.i2 = __shfl_xor(v.i2, off, kWave);
     v = top2_merge(v, o);
   }
-  if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = v;
-  __syncthreads();
-  Top2 r = sh[0];
-  for (int w = 1; w < kWavesPerBlock; ++w) r = top2_merge(r, sh[w]);
-  __syncthreads();
-  return r;
+  return v;
 }
 
-// Exponential-race keys of 8 ids: E_v / w_v with E_v = -log2 u_v (a constant
-// factor ln 2 does not change the argmin) and w_v the unnormalised weight.
-// residual: w = p - q with p = 2^(z_t*k2 - L2t), q = p * 2^((z_d - z_t)*k2 + D2)
-// bonus (or empty-residual fallback): w = p.
-template <int DT, bool VEC>
-__device__ __forceinline__ void scan_group(const void* row_t, const void* row_d, bool residual,
-                                           int64_t e0, int64_t end, float k2, float L2t, float D2,
-                                           uint32_t pos, uint32_t r, uint32_t s0, uint32_t s1,
-                                           Top2& best) {
-  float zt[kGroup], zd[kGroup];
-  load8<DT, VEC>(row_t, e0, end, zt);
-  if (residual) load8<DT, VEC>(row_d, e0, end, zd);
-  const uint32_t c0 = uint32_t(e0 >> 2);
-  const Philox4 lo = philox4x32_10(c0, pos, r, kPurposeSample, s0, s1);
-  const Philox4 hi = philox4x32_10(c0 + 1u, pos, r, kPurposeSample, s0, s1);
+// What a scan needs to know about the draw.
+struct DrawParams {
+  float k2;     // log2(e) / T
+  float L2t;    // ln Z of the target row, in log2 units
+  float D2;     // (ln Z_t - ln Z_d) in log2 units (residual draws)
+  uint32_t pos, r, s0, s1;
+};
+
+// Exponential-race keys of the 8 ids of vector vi: key_v = E_v / w_v with
+// E_v = -log2 u_v (a constant factor ln 2 does not move the argmin) and w_v
+// the unnormalised weight, 2^(z_t*k2 - L2t) = p_v for the bonus draw, and
+// p_v - q_v with q_v = p_v * 2^((z_d - z_t)*k2 + D2) for the residual draw.
+// PARTIAL: vi is a row's last, partial vector; ids >= V are skipped.
+template <int DT, bool RESIDUAL, bool PARTIAL>
+__device__ __forceinline__ void score_vec(const RawVec<DT>& rt, const RawVec<DT>& rd, int64_t vi,
+                                          int64_t V, const DrawParams& dp, Top2& best) {
+  const uint32_t c0 = uint32_t(vi * 2);
+  const Philox4 lo = philox4x32_10(c0, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
+  const Philox4 hi = philox4x32_10(c0 + 1u, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
 #pragma unroll
-  for (int t = 0; t < kGroup; ++t) {
-    const float a2 = fmaf(zt[t], k2, -L2t);
-    const float p = __builtin_amdgcn_exp2f(a2);
-    float w = p;
-    if (residual) w = p - __builtin_amdgcn_exp2f(a2 + fmaf(zd[t] - zt[t], k2, D2));
+  for (int t = 0; t < kVec; ++t) {
+    const float zt = vec_elem<DT>(rt, t);
+    const float a2 = fmaf(zt, dp.k2, -dp.L2t);
+    float w = __builtin_amdgcn_exp2f(a2);
+    if constexpr (RESIDUAL)
+      w -= __builtin_amdgcn_exp2f(a2 + fmaf(vec_elem<DT>(rd, t) - zt, dp.k2, dp.D2));
     const uint32_t word = t < 4 ? lo.w[t] : hi.w[t - 4];
     const float e2 = -__builtin_amdgcn_logf(unit_uniform(word));
-    const float key = (w > 0.0f) ? e2 * __builtin_amdgcn_rcpf(w) : INFINITY;
-    if (e0 + t < end) top2_insert(best, key, int32_t(e0 + t));
+    float key = (w > 0.0f) ? e2 * __builtin_amdgcn_rcpf(w) : INFINITY;
+    if constexpr (PARTIAL) key = (vi * kVec + t < V) ? key : INFINITY;
+    top2_push(best, key, int32_t(vi * kVec + t));
   }
 }
 
@@ -548,95 +746,309 @@ __device__ double rescore(const void* row_t, const void* row_d, bool residual, i
   return lp + log(-expm1(dd)) + g;
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void sample_kernel(SampleArgs a) {
-  constexpr int esz = DT == SV_BF16 ? 2 : 4;
-  __shared__ Top2 sh[kWavesPerBlock];
-  __shared__ int s_last;
-  const int64_t chain = blockIdx.x / a.nsplit;
-  const int64_t split = blockIdx.x - chain * a.nsplit;
-  const int64_t b = chain / a.K;
-  const int64_t k = chain - b * a.K;
-  const int G = int(a.G);
-  const int n = a.accept_len[chain];
-  const float T = a.temp[b];
-  if (n < 0 || n > G) return;
-  if (!(T > 0.0f)) {
-    if (T == 0.0f && a.amax_t && split == 0 && threadIdx.x == 0)
-      a.out_token[chain] = a.amax_t[b * (G + 1) + n];
-    return;
+// Scan vectors vi0 + kBlock*it (it < kSampleIters) of the row pair: the loads of
+// all iterations are issued before any is scored.
+template <int DT, bool VEC, bool RESIDUAL>
+__device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d, int64_t vi0,
+                                           int64_t V, const DrawParams& dp) {
+  const int64_t vpr = (V + kVec - 1) / kVec;
+  const bool partial_tail = (V % kVec) != 0;
+  RawVec<DT> rt[kSampleIters], rd[kSampleIters];
+#pragma unroll
+  for (int it = 0; it < kSampleIters; ++it) {
+    const int64_t vi = vi0 + int64_t(kBlock) * it;
+    const bool inside = vi < vpr;
+    rt[it] = inside ? load_vec_bounded<DT, VEC>(row_t, vi, V) : neg_inf_vec<DT>();
+    if constexpr (RESIDUAL) rd[it] = inside ? load_vec_bounded<DT, VEC>(row_d, vi, V) : rt[it];
   }
-  const bool residual = n < G;
-  const void* row_t = row_ptr(a.t, esz, b * a.tsb + int64_t(n) * a.tsj);
-  const void* row_d = residual ? row_ptr(a.d, esz, b * a.dsb + k * a.dsk + int64_t(n) * a.dsj)
-                               : nullptr;
-  const double lzt = a.lnz_t[b * (G + 1) + n];
-  const double lzd = residual ? a.lnz_d[(b * a.K + k) * G + n] : 0.0;
-  const float k2 = kLog2e / T;
-  const float L2t = float(lzt * kLog2eD);
-  const float D2 = residual ? float((lzt - lzd) * kLog2eD) : 0.0f;
-  const uint32_t pos = uint32_t(uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(n));
-  const uint32_t r = uint32_t(chain);
-  const uint32_t s0 = uint32_t(a.seed), s1 = uint32_t(a.seed >> 32);
-
-  const int64_t start = split * kSplit;
-  const int64_t end = start + kSplit < a.V ? start + kSplit : a.V;
   Top2 best = top2_empty();
 #pragma unroll
   for (int it = 0; it < kSampleIters; ++it) {
-    const int64_t e0 = start + int64_t(kGroup) * (threadIdx.x + int64_t(kBlock) * it);
-    if (e0 < end)
-      scan_group<DT, VEC>(row_t, row_d, residual, e0, end, k2, L2t, D2, pos, r, s0, s1, best);
-  }
-  best = block_top2(best, sh);
-
-  if (threadIdx.x == 0) {
-    a.part[chain * a.nsplit + split] = best;
-    __threadfence();
-    const uint32_t prev = atomicAdd(a.cnt + chain, 1u);
-    s_last = prev == uint32_t(a.nsplit - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // Last workgroup of the chain: merge the splits in order.
-  Top2 all = top2_empty();
-  if (threadIdx.x == 0) {
-    for (int64_t s = 0; s < a.nsplit; ++s) {
-      const Top2 p = a.part[chain * a.nsplit + s];
-      all = top2_merge(all, p);
+    const int64_t vi = vi0 + int64_t(kBlock) * it;
+    if (vi < vpr) {
+      if (partial_tail && vi == vpr - 1)
+        score_vec<DT, RESIDUAL, true>(rt[it], RESIDUAL ? rd[it] : rt[it], vi, V, dp, best);
+      else
+        score_vec<DT, RESIDUAL, false>(rt[it], RESIDUAL ? rd[it] : rt[it], vi, V, dp, best);
     }
-    a.cnt[chain] = 0u;
-    sh[0] = all;
   }
-  __syncthreads();
-  all = sh[0];
-  __syncthreads();
-  bool use_residual = residual;
-  if (all.k1 == INFINITY && residual) {
-    // Empty residual support (rounding only): draw from p_n with the same noise.
-    use_residual = false;
-    Top2 fb = top2_empty();
-    for (int64_t e0 = int64_t(kGroup) * threadIdx.x; e0 < a.V; e0 += int64_t(kGroup) * kBlock)
-      scan_group<DT, VEC>(row_t, row_d, false, e0, a.V, k2, L2t, D2, pos, r, s0, s1, fb);
-    all = block_top2(fb, sh);
+  return best;
+}
+
+struct ChainArgs {
+  RowSet rs;
+  int64_t V;
+  Partition p;               // stream partition (compact mode: nrows/N taken from rank[B])
+  int compact;
+  const RowPartial* part;
+  const int32_t* rank;       // [B + 1] (compact mode)
+  const int32_t* tokens;     // [B, K, G]
+  uint64_t seed;
+  const int64_t* pos0;
+  // outputs (written by split 0)
+  int32_t* accept_len;
+  int32_t* out_token;
+  float* logp;
+  float* logq;
+  double* lnz_t_out;
+  double* lnz_d_out;
+  int32_t* dev_err;
+  // given-n mode (specverify_residual_sample)
+  const double* lnz_t_in;    // [B, G+1]
+  const double* lnz_d_in;    // [B, K, G]
+  const int32_t* amax_in;    // [B, G+1]
+  const int32_t* n_in;       // [B, K]
+  // to the finish kernel
+  int64_t nsplit;
+  Cand* cand;                // [B*K][nsplit]
+  ChainInfo* info;           // [B*K]
+};
+
+// At least 4 waves per SIMD: a 256-thread workgroup per (chain, split) then
+// fits 16 workgroups' worth of waves per CU, so the usual grids run in one round.
+template <int DT, bool VEC, bool GIVEN>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void chain_kernel(ChainArgs a) {
+  constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  __shared__ double s_lnz[kMaxRowsPerChain];
+  __shared__ int32_t s_amax[SV_MAX_GAMMA + 1];
+  __shared__ int32_t s_bad;
+  __shared__ int32_t s_n;
+  __shared__ Top2 s_top[kWavesPerBlock];
+  const RowSet& rs = a.rs;
+  const int64_t chain = blockIdx.x / a.nsplit;
+  const int64_t split = blockIdx.x - chain * a.nsplit;
+  const int64_t b = chain / rs.K;
+  const int64_t k = chain - b * rs.K;
+  const int G = int(rs.G);
+  const int P = G + 1;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const float T = rs.temp[b];
+  const bool sampled = T > 0.0f;
+  const bool greedy = T == 0.0f;
+  const bool lead = split == 0;
+
+  if (GIVEN) {
+    if (t == 0) {
+      const int32_t n = a.n_in[chain];
+      s_n = (n < 0 || n > G) ? -1 : n;
+    }
+    if (t < P) {
+      s_lnz[t] = a.lnz_t_in[b * P + t];
+      s_amax[t] = a.amax_in[b * P + t];
+    }
+    if (t < G) s_lnz[P + t] = a.lnz_d_in[chain * G + t];
+    __syncthreads();
+    if (greedy && lead && t == 0 && s_n >= 0) a.out_token[chain] = s_amax[s_n];
+  } else {
+    Partition p = a.p;
+    if (a.compact) {
+      p.nrows = rs.B * P + int64_t(a.rank[rs.B]) * rs.K * G;
+      p.N = p.nrows * p.vpr;
+    }
+    // Loads that do not depend on the normalisers go first so their latency
+    // overlaps the merges: draft tokens, the logits at them, accept uniforms.
+    int32_t x = 0;
+    bool tok_bad = false;
+    float zt = 0.0f, zd = 0.0f;
+    double log_u = 0.0;
+    if (t < G) {
+      x = a.tokens[chain * G + t];
+      tok_bad = x < 0 || int64_t(x) >= a.V;
+      if (!tok_bad && sampled) {
+        zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + t * rs.tsj), x);
+        zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + t * rs.dsj), x);
+      }
+      const uint64_t pos = uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(t);
+      const Philox4 r = philox4x32_10(0u, uint32_t(pos), uint32_t(chain), kPurposeAccept,
+                                      uint32_t(a.seed), uint32_t(a.seed >> 32));
+      log_u = log_uniform_d(unit_uniform_d(r.w[0]));
+    }
+    if (t == 0) s_bad = 0;
+    __syncthreads();
+    // normalisers of the chain's rows: target rows 0..G, then draft rows (k, 0..G-1)
+    if (t < P + G) {
+      const bool is_draft = t >= P;
+      double lnz = NAN;
+      if (!is_draft || sampled) {
+        int64_t rho;
+        if (!is_draft) {
+          rho = b * P + t;
+        } else {
+          const int64_t sb = a.compact ? int64_t(a.rank[b]) : b;
+          rho = rs.B * P + sb * rs.K * G + k * G + (t - P);
+        }
+        const RowStat r = merge_row<4>(a.part, p, rho, T);
+        lnz = r.lnz;
+        if (!(r.m > -INFINITY)) atomicOr(&s_bad, SV_ERR_ROW);
+        if (!is_draft) s_amax[t] = r.idx == INT_MAX ? 0 : r.idx;
+      }
+      s_lnz[t] = lnz;
+      if (lead) {
+        if (!is_draft && k == 0 && a.lnz_t_out) a.lnz_t_out[b * P + t] = lnz;
+        if (is_draft && sampled && a.lnz_d_out) a.lnz_d_out[chain * G + (t - P)] = lnz;
+      }
+    }
+    __syncthreads();
+    // accept tests of the G positions in wavefront 0, first rejection by ballot
+    if (t < kWave) {
+      bool acc = false;
+      if (t < G) {
+        const int j = t;
+        double lp = 0.0, lq = 0.0;
+        if (!tok_bad) {
+          if (sampled) {
+            lp = double(zt) / double(T) - s_lnz[j];
+            lq = double(zd) / double(T) - s_lnz[P + j];
+            acc = log_u < lp - lq;
+          } else if (greedy) {
+            acc = x == s_amax[j];
+            lp = acc ? 0.0 : -INFINITY;
+            lq = 0.0;
+          }
+        }
+        if (lead && a.logp) a.logp[chain * G + j] = float(lp);
+        if (lead && a.logq) a.logq[chain * G + j] = float(lq);
+      }
+      const uint64_t acc_mask = __ballot(acc);
+      const uint64_t bad_mask = __ballot(tok_bad);
+      if (t == 0) {
+        const int n = __builtin_ctzll(~acc_mask);  // leading accepts (<= G: bit G of ~mask is set)
+        int32_t err = s_bad;
+        if (bad_mask) err |= SV_ERR_TOKEN;
+        if (!(sampled || greedy)) err |= SV_ERR_TEMP;
+        s_n = err ? -1 : n;
+        if (lead) {
+          if (err) {
+            a.accept_len[chain] = -1;
+            a.out_token[chain] = -1;
+            if (a.dev_err) atomicOr(a.dev_err, err);
+          } else {
+            a.accept_len[chain] = n;
+            if (greedy) a.out_token[chain] = s_amax[n];
+          }
+        }
+      }
+    }
+    __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    const double s1d = rescore<DT>(row_t, row_d, use_residual, all.i1, double(T), lzt, lzd, pos,
-                                   r, s0, s1);
-    const double s2d = rescore<DT>(row_t, row_d, use_residual, all.i2, double(T), lzt, lzd, pos,
-                                   r, s0, s1);
-    int32_t win = all.i1;
-    if (s2d > s1d || (s2d == s1d && all.i2 < all.i1)) win = all.i2;
-    if (win == INT_MAX) win = -1;
-    a.out_token[chain] = win;
+
+  const int n = s_n;
+  if (lead && t == 0) {
+    ChainInfo ci;
+    ci.n = (n >= 0 && sampled) ? n : -1;
+    ci.lzt = n >= 0 ? s_lnz[n] : 0.0;
+    ci.lzd = (n >= 0 && n < G) ? s_lnz[P + n] : 0.0;
+    ci.pad[0] = ci.pad[1] = ci.pad[2] = 0;
+    a.info[chain] = ci;
+  }
+  if (n < 0 || !sampled) return;  // uniform across the workgroup
+
+  // Scan this split of the row pair, then re-score its best two in float64.
+  const bool residual = n < G;
+  const void* row_t = row_ptr(rs.t, esz, b * rs.tsb + int64_t(n) * rs.tsj);
+  const void* row_d =
+      residual ? row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + int64_t(n) * rs.dsj) : row_t;
+  const double lzt = s_lnz[n];
+  const double lzd = residual ? s_lnz[P + n] : 0.0;
+  DrawParams dp;
+  dp.k2 = kLog2e / T;
+  dp.L2t = float(lzt * kLog2eD);
+  dp.D2 = residual ? float((lzt - lzd) * kLog2eD) : 0.0f;
+  dp.pos = uint32_t(uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(n));
+  dp.r = uint32_t(chain);
+  dp.s0 = uint32_t(a.seed);
+  dp.s1 = uint32_t(a.seed >> 32);
+  const int64_t vi0 = split * (kSplit / kVec) + t;
+  Top2 best = residual ? scan_split<DT, VEC, true>(row_t, row_d, vi0, a.V, dp)
+                       : scan_split<DT, VEC, false>(row_t, row_d, vi0, a.V, dp);
+  best = wave_top2(best);
+  if (lane == 0) s_top[t / kWave] = best;
+  __syncthreads();
+  if (t < kWave) {
+    Top2 all = s_top[0];
+    for (int w = 1; w < kWavesPerBlock; ++w) all = top2_merge(all, s_top[w]);
+    // lanes 0 and 1 re-score the two candidates side by side
+    const int32_t id = lane == 0 ? all.i1 : all.i2;
+    double sc = -INFINITY;
+    if (lane < 2)
+      sc = rescore<DT>(row_t, row_d, residual, id, double(T), lzt, lzd, dp.pos, dp.r, dp.s0, dp.s1);
+    const double sc2 = __shfl(sc, 1, kWave);
+    if (lane == 0) {
+      Cand c{sc, all.i1, 0};
+      if (sc2 > sc || (sc2 == sc && all.i2 < all.i1)) c = Cand{sc2, all.i2, 0};
+      if (c.score == -INFINITY) c.id = INT_MAX;
+      a.cand[chain * a.nsplit + split] = c;
+    }
   }
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+// One wavefront per chain: the best float64 score over the splits wins (ties
+// to the lowest id). No candidate anywhere means an empty residual support
+// (reachable only by rounding): the token is then drawn from p_n with the same
+// noise by a pass over the whole row.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kWave) void finish_kernel(const void* tgt, int64_t tsb, int64_t tsj,
+                                                       int64_t K, int64_t G, int64_t V,
+                                                       const float* __restrict__ temp,
+                                                       uint64_t seed, const int64_t* pos0,
+                                                       const ChainInfo* __restrict__ info,
+                                                       const Cand* __restrict__ cand,
+                                                       int64_t nsplit,
+                                                       int32_t* __restrict__ out_token) {
+  constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  const int64_t chain = blockIdx.x;
+  const ChainInfo ci = info[chain];
+  const int n = ci.n;
+  if (n < 0) return;
+  const int lane = threadIdx.x;
+  double best = -INFINITY;
+  int32_t id = INT_MAX;
+  for (int64_t sp = lane; sp < nsplit; sp += kWave) {
+    const Cand c = cand[chain * nsplit + sp];
+    if (c.score > best || (c.score == best && c.id < id)) {
+      best = c.score;
+      id = c.id;
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const double ob = __shfl_xor(best, off, kWave);
+    const int32_t oi = __shfl_xor(id, off, kWave);
+    if (ob > best || (ob == best && oi < id)) {
+      best = ob;
+      id = oi;
+    }
+  }
+  if (id == INT_MAX) {
+    const int64_t b = chain / K;
+    const float T = temp[b];
+    const void* row_t = row_ptr(tgt, esz, b * tsb + int64_t(n) * tsj);
+    DrawParams dp;
+    dp.k2 = kLog2e / T;
+    dp.L2t = float(ci.lzt * kLog2eD);
+    dp.D2 = 0.0f;
+    dp.pos = uint32_t(uint64_t(pos0 ? pos0[b] : 0) + uint64_t(n));
+    dp.r = uint32_t(chain);
+    dp.s0 = uint32_t(seed);
+    dp.s1 = uint32_t(seed >> 32);
+    const int64_t vpr = (V + kVec - 1) / kVec;
+    Top2 fb = top2_empty();
+    for (int64_t vi = lane; vi < vpr; vi += kWave) {
+      const RawVec<DT> pt = load_vec_bounded<DT, VEC>(row_t, vi, V);
+      score_vec<DT, false, true>(pt, pt, vi, V, dp, fb);
+    }
+    fb = wave_top2(fb);
+    double sc = -INFINITY;
+    if (lane < 2)
+      sc = rescore<DT>(row_t, row_t, false, lane == 0 ? fb.i1 : fb.i2, double(T), ci.lzt, 0.0,
+                       dp.pos, dp.r, dp.s0, dp.s1);
+    const double sc2 = __shfl(sc, 1, kWave);
+    id = fb.i1;
+    if (sc2 > sc || (sc2 == sc && fb.i2 < fb.i1)) id = fb.i2;
+  }
+  if (lane == 0) out_token[chain] = id == INT_MAX ? -1 : id;
 }
 
 // ---------------------------------------------------------------------------
@@ -667,114 +1079,148 @@ __global__ __launch_bounds__(kBlock) void accept_scalar_kernel(const float* __re
 // ---------------------------------------------------------------------------
 // Host side.
 
-struct Layout {
-  int64_t nch, clen, rows, chains, nsplit;
-  size_t off_part, off_lnz, off_top, off_cnt, total;
-};
-
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int64_t chunks_per_row(int64_t V) { return (V + kUnit - 1) / kUnit; }
-int64_t chunk_len(int64_t V) {
-  const int64_t n = chunks_per_row(V);
-  const int64_t l = (V + n - 1) / n;
-  return (l + kGroup - 1) / kGroup * kGroup;
-}
+struct Layout {
+  int64_t vpr, nrows, chains, nsplit, part_slots;
+  size_t off_part, off_rank, off_info, off_top, total;
+};
 
-Layout make_layout(int64_t rows, int64_t chains, int64_t V) {
+// part_slots bounds W * maxseg for every W <= kMaxWaves: maxseg(W) <= N/(W*vpr) + 3.
+Layout make_layout(int64_t B, int64_t nrows, int64_t chains, int64_t V) {
   Layout L;
-  L.nch = chunks_per_row(V);
-  L.clen = chunk_len(V);
-  L.rows = rows;
+  L.vpr = (V + kVec - 1) / kVec;
+  L.nrows = nrows;
   L.chains = chains;
   L.nsplit = (V + kSplit - 1) / kSplit;
+  L.part_slots = nrows + 3 * kMaxWaves;
   L.off_part = 0;
-  L.off_lnz = align256(L.off_part + size_t(rows) * size_t(L.nch) * sizeof(RowPartial));
-  L.off_top = align256(L.off_lnz + size_t(rows) * sizeof(double));
-  L.off_cnt = align256(L.off_top + size_t(chains) * size_t(L.nsplit) * sizeof(Top2));
-  L.total = align256(L.off_cnt + size_t(chains) * sizeof(uint32_t));
+  L.off_rank = align256(L.off_part + size_t(L.part_slots) * sizeof(RowPartial));
+  L.off_info = align256(L.off_rank + size_t(B + 1) * sizeof(int32_t));
+  L.off_top = align256(L.off_info + size_t(chains) * sizeof(ChainInfo));
+  L.total = align256(L.off_top + size_t(chains) * size_t(L.nsplit) * sizeof(Cand));
   return L;
 }
 
-int device_cu_count() {
-  static int cached[64] = {0};
+Partition make_partition(const Layout& L, int64_t W) {
+  Partition p;
+  p.vpr = L.vpr;
+  p.nrows = L.nrows;
+  p.N = L.nrows * L.vpr;
+  p.W = W;
+  const int64_t range = (p.N + W - 1) / W;
+  p.maxseg = range / L.vpr + 2;
+  return p;
+}
+
+// Wavefronts of one stream-kernel instantiation that fit on the device at once
+// (cached per device; only balance depends on it, never correctness).
+template <int DT, bool VEC, bool ARGMAX_ALL>
+int64_t stream_waves() {
+  static std::atomic<int64_t> cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    n = 256;
-  if (dev < 64) cached[dev] = n;
-  return n;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<DT, VEC, ARGMAX_ALL>,
+                                                   kBlock, 0) != hipSuccess ||
+      blocks <= 0)
+    blocks = 4;
+  int64_t w = int64_t(cus) * blocks * kWavesPerBlock;
+  if (w > kMaxWaves) w = kMaxWaves;
+  w -= w % kWavesPerBlock;
+  if (dev < 64) cache[dev].store(w, std::memory_order_relaxed);
+  return w;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool stride_ok(int64_t s, int esz) { return (s * esz) % 16 == 0; }
-
 int check_dtype(int dtype) { return (dtype == SV_F32 || dtype == SV_BF16) ? SV_OK : SV_EDTYPE; }
 int esize(int dtype) { return dtype == SV_BF16 ? 2 : 4; }
-
 int launch_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP; }
 
-template <int DT, bool VEC>
-void launch_rowstats_t(const RowSet& rs, int64_t V, const Layout& L, RowPartial* part,
-                       bool argmax_all, hipStream_t st) {
-  const int64_t units = L.rows * L.nch;
-  int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t cap = int64_t(device_cu_count()) * 8;
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  if (argmax_all)
-    hipLaunchKernelGGL((rowstats_kernel<DT, VEC, true>), dim3(unsigned(blocks)), dim3(kBlock), 0,
-                       st, rs, V, L.nch, L.clen, units, part);
-  else
-    hipLaunchKernelGGL((rowstats_kernel<DT, VEC, false>), dim3(unsigned(blocks)), dim3(kBlock), 0,
-                       st, rs, V, L.nch, L.clen, units, part);
+template <int DT, bool VEC, bool ARGMAX_ALL>
+Partition launch_stream_t(StreamArgs sa, const Layout& L, hipStream_t st) {
+  const int64_t W = stream_waves<DT, VEC, ARGMAX_ALL>();
+  sa.p = make_partition(L, W);
+  hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(W / kWavesPerBlock)),
+                     dim3(kBlock), 0, st, sa);
+  return sa.p;
 }
 
-void launch_rowstats(int dtype, bool vec, const RowSet& rs, int64_t V, const Layout& L,
-                     RowPartial* part, bool argmax_all, hipStream_t st) {
+// Returns the partition the merge kernels must use (in compact mode they
+// replace nrows and N by the counts the stream kernel wrote to rank[B]).
+Partition launch_stream(int dtype, bool vec, bool argmax_all, const StreamArgs& sa,
+                        const Layout& L, hipStream_t st) {
   if (dtype == SV_BF16) {
-    if (vec) launch_rowstats_t<SV_BF16, true>(rs, V, L, part, argmax_all, st);
-    else launch_rowstats_t<SV_BF16, false>(rs, V, L, part, argmax_all, st);
-  } else {
-    if (vec) launch_rowstats_t<SV_F32, true>(rs, V, L, part, argmax_all, st);
-    else launch_rowstats_t<SV_F32, false>(rs, V, L, part, argmax_all, st);
+    if (vec) return argmax_all ? launch_stream_t<SV_BF16, true, true>(sa, L, st)
+                               : launch_stream_t<SV_BF16, true, false>(sa, L, st);
+    return argmax_all ? launch_stream_t<SV_BF16, false, true>(sa, L, st)
+                      : launch_stream_t<SV_BF16, false, false>(sa, L, st);
   }
+  if (vec) return argmax_all ? launch_stream_t<SV_F32, true, true>(sa, L, st)
+                             : launch_stream_t<SV_F32, true, false>(sa, L, st);
+  return argmax_all ? launch_stream_t<SV_F32, false, true>(sa, L, st)
+                    : launch_stream_t<SV_F32, false, false>(sa, L, st);
 }
 
-void launch_sample(int dtype, bool vec, const SampleArgs& sa, hipStream_t st) {
-  const int64_t blocks = sa.B * sa.K * sa.nsplit;
-  const dim3 grid{unsigned(blocks), 1u, 1u};
+template <int DT, bool VEC>
+void launch_chain_finish(const ChainArgs& ca, bool given, hipStream_t st) {
+  const int64_t chains = ca.rs.B * ca.rs.K;
+  const dim3 grid{unsigned(chains * ca.nsplit), 1u, 1u};
+  if (given) hipLaunchKernelGGL((chain_kernel<DT, VEC, true>), grid, dim3(kBlock), 0, st, ca);
+  else hipLaunchKernelGGL((chain_kernel<DT, VEC, false>), grid, dim3(kBlock), 0, st, ca);
+  const RowSet& rs = ca.rs;
+  hipLaunchKernelGGL((finish_kernel<DT, VEC>), dim3(unsigned(chains)), dim3(kWave), 0, st, rs.t,
+                     rs.tsb, rs.tsj, rs.K, rs.G, ca.V, rs.temp, ca.seed, ca.pos0, ca.info,
+                     ca.cand, ca.nsplit, ca.out_token);
+}
+
+void launch_chain(int dtype, bool vec, const ChainArgs& ca, bool given, hipStream_t st) {
   if (dtype == SV_BF16) {
-    if (vec) hipLaunchKernelGGL((sample_kernel<SV_BF16, true>), grid, dim3(kBlock), 0, st, sa);
-    else hipLaunchKernelGGL((sample_kernel<SV_BF16, false>), grid, dim3(kBlock), 0, st, sa);
+    if (vec) launch_chain_finish<SV_BF16, true>(ca, given, st);
+    else launch_chain_finish<SV_BF16, false>(ca, given, st);
   } else {
-    if (vec) hipLaunchKernelGGL((sample_kernel<SV_F32, true>), grid, dim3(kBlock), 0, st, sa);
-    else hipLaunchKernelGGL((sample_kernel<SV_F32, false>), grid, dim3(kBlock), 0, st, sa);
+    if (vec) launch_chain_finish<SV_F32, true>(ca, given, st);
+    else launch_chain_finish<SV_F32, false>(ca, given, st);
   }
 }
 
 bool sizes_ok(int64_t B, int64_t K, int64_t G, int64_t V) {
-  return B >= 1 && K >= 1 && G >= 1 && G <= SV_MAX_GAMMA && K * G <= SV_MAX_CHAIN_DECISIONS &&
-         V >= 1 && V < (int64_t(1) << 31) && B * K < (int64_t(1) << 31) &&
-         B <= (int64_t(1) << 31) / (G + 1);
+  if (!(B >= 1 && K >= 1 && G >= 1 && G <= SV_MAX_GAMMA && K * G <= SV_MAX_CHAIN_DECISIONS &&
+        V >= 1 && V < (int64_t(1) << 31)))
+    return false;
+  const int64_t nsplit = (V + kSplit - 1) / kSplit;
+  return B <= (int64_t(1) << 31) / (G + 1) / (K + 1) && B * K * nsplit < (int64_t(1) << 31);
 }
 
 bool workspace_ok(void* ws, size_t have, size_t need, int* status) {
-  if (need > 0 && (ws == nullptr || have < need)) {
+  if (ws == nullptr || have < need) {
     *status = SV_EWORKSPACE;
     return false;
   }
-  if (ws && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) {
     *status = SV_EALIGN;
     return false;
   }
   return true;
 }
 
-size_t step_workspace(int64_t B, int64_t K, int64_t G, int64_t V) {
-  return make_layout(B * (G + 1) + B * K * G, B * K, V).total;
+Layout step_layout(int64_t B, int64_t K, int64_t G, int64_t V) {
+  return make_layout(B, B * (G + 1) + B * K * G, B * K, V);
+}
+
+bool logits_vec_ok(const void* t, const void* d, int esz, int64_t tsb, int64_t tsj, int64_t dsb,
+                   int64_t dsk, int64_t dsj) {
+  return aligned16(t) && aligned16(d) && stride_ok(tsb, esz) && stride_ok(tsj, esz) &&
+         stride_ok(dsb, esz) && stride_ok(dsk, esz) && stride_ok(dsj, esz);
 }
 
 }  // namespace
@@ -784,11 +1230,13 @@ extern "C" {
 size_t specverify_workspace_size(int64_t B, int64_t K, int64_t gamma, int64_t V, int dtype) {
   if (check_dtype(dtype) != SV_OK) return 0;
   if (K == 0) {  // specverify_normalize: P = gamma + 1 rows per batch row
-    if (B < 1 || gamma < 0 || V < 1 || V >= (int64_t(1) << 31)) return 0;
-    return make_layout(B * (gamma + 1), 0, V).total;
+    if (B < 1 || gamma < 0 || V < 1 || V >= (int64_t(1) << 31) ||
+        B > (int64_t(1) << 40) / (gamma + 1))
+      return 0;
+    return make_layout(B, B * (gamma + 1), 0, V).total;
   }
   if (!sizes_ok(B, K, gamma, V)) return 0;
-  return step_workspace(B, K, gamma, V);
+  return step_layout(B, K, gamma, V).total;
 }
 
 int specverify_normalize(const void* logits, int dtype, int64_t B, int64_t P, int64_t V,
@@ -796,22 +1244,28 @@ int specverify_normalize(const void* logits, int dtype, int64_t B, int64_t P, in
                          double* lnZ, int32_t* argmax, void* workspace, size_t workspace_bytes,
                          void* stream) {
   if (!logits || !temperature || !lnZ) return SV_EINVAL;
-  if (B < 1 || P < 1 || V < 1 || V >= (int64_t(1) << 31) || stride_b < 0 || stride_p < 0)
+  if (B < 1 || P < 1 || V < 1 || V >= (int64_t(1) << 31) || stride_b < 0 || stride_p < 0 ||
+      B > (int64_t(1) << 40) / P)
     return SV_EINVAL;
   if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
-  const Layout L = make_layout(B * P, 0, V);
+  const Layout L = make_layout(B, B * P, 0, V);
   int status = SV_OK;
   if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
   const int esz = esize(dtype);
   const bool vec = aligned16(logits) && stride_ok(stride_b, esz) && stride_ok(stride_p, esz);
-  RowSet rs{logits, stride_b, stride_p, nullptr, 0, 0, 0, B, P, 0, 1, temperature};
   auto* base = reinterpret_cast<char*>(workspace);
   auto* part = reinterpret_cast<RowPartial*>(base + L.off_part);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  launch_rowstats(dtype, vec, rs, V, L, part, argmax != nullptr, st);
-  const int64_t rows = B * P;
-  hipLaunchKernelGGL(finalize_rows_kernel, dim3(unsigned((rows + kBlock - 1) / kBlock)),
-                     dim3(kBlock), 0, st, part, rows, P, L.nch, temperature, lnZ, argmax);
+  StreamArgs sa{};
+  sa.rs = RowSet{logits, stride_b, stride_p, nullptr, 0, 0, 0, B, P, 0, 1, temperature};
+  sa.V = V;
+  sa.compact = 0;
+  sa.part = part;
+  sa.rank_out = nullptr;
+  const Partition p = launch_stream(dtype, vec, argmax != nullptr, sa, L, st);
+  hipLaunchKernelGGL(finalize_rows_kernel,
+                     dim3(unsigned((B * P + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kBlock), 0,
+                     st, part, p, P, temperature, lnZ, argmax);
   return launch_status();
 }
 
@@ -819,7 +1273,7 @@ int specverify_accept(const float* logp, const float* logq, int64_t B, int64_t K
                       uint64_t seed, const int64_t* pos0, int32_t* accept_len,
                       uint32_t* accept_bits, void* stream) {
   if (!logp || !logq || !accept_len) return SV_EINVAL;
-  if (B < 1 || K < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || B * K >= (int64_t(1) << 31))
+  if (B < 1 || K < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || B > (int64_t(1) << 31) / K)
     return SV_EINVAL;
   const int64_t n = B * K;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -843,25 +1297,29 @@ int specverify_residual_sample(const void* target_logits, const void* draft_logi
   if (t_stride_b < 0 || t_stride_j < 0 || d_stride_b < 0 || d_stride_k < 0 || d_stride_j < 0)
     return SV_EINVAL;
   if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
-  const Layout L = make_layout(B * (gamma + 1) + B * K * gamma, B * K, V);
+  const Layout L = step_layout(B, K, gamma, V);
   int status = SV_OK;
   if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
   const int esz = esize(dtype);
-  const bool vec = aligned16(target_logits) && aligned16(draft_logits) &&
-                   stride_ok(t_stride_b, esz) && stride_ok(t_stride_j, esz) &&
-                   stride_ok(d_stride_b, esz) && stride_ok(d_stride_k, esz) &&
-                   stride_ok(d_stride_j, esz);
+  const bool vec = logits_vec_ok(target_logits, draft_logits, esz, t_stride_b, t_stride_j,
+                                 d_stride_b, d_stride_k, d_stride_j);
   auto* base = reinterpret_cast<char*>(workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  auto* cnt = reinterpret_cast<uint32_t*>(base + L.off_cnt);
-  const int64_t chains = B * K;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(unsigned((chains + kBlock - 1) / kBlock)), dim3(kBlock),
-                     0, st, cnt, chains);
-  SampleArgs sa{target_logits, t_stride_b, t_stride_j, draft_logits, d_stride_b, d_stride_k,
-                d_stride_j, B, K, gamma, V, temperature, lnZ_target, lnZ_draft, argmax_target,
-                accept_len, seed, pos0, out_token, L.nsplit,
-                reinterpret_cast<Top2*>(base + L.off_top), cnt};
-  launch_sample(dtype, vec, sa, st);
+  ChainArgs ca{};
+  ca.rs = RowSet{target_logits, t_stride_b, t_stride_j, draft_logits, d_stride_b, d_stride_k,
+                 d_stride_j, B, gamma + 1, K, gamma, temperature};
+  ca.V = V;
+  ca.seed = seed;
+  ca.pos0 = pos0;
+  ca.out_token = out_token;
+  ca.lnz_t_in = lnZ_target;
+  ca.lnz_d_in = lnZ_draft;
+  ca.amax_in = argmax_target;
+  ca.n_in = accept_len;
+  ca.nsplit = L.nsplit;
+  ca.cand = reinterpret_cast<Cand*>(base + L.off_top);
+  ca.info = reinterpret_cast<ChainInfo*>(base + L.off_info);
+  launch_chain(dtype, vec, ca, true, st);
   return launch_status();
 }
 
@@ -880,36 +1338,49 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
   if (t_stride_b < 0 || t_stride_j < 0 || d_stride_b < 0 || d_stride_k < 0 || d_stride_j < 0)
     return SV_EINVAL;
   if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
-  const Layout L = make_layout(B * (gamma + 1) + B * K * gamma, B * K, V);
+  const Layout L = step_layout(B, K, gamma, V);
   int status = SV_OK;
   if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
   const int esz = esize(dtype);
-  const bool vec = aligned16(target_logits) && aligned16(draft_logits) &&
-                   stride_ok(t_stride_b, esz) && stride_ok(t_stride_j, esz) &&
-                   stride_ok(d_stride_b, esz) && stride_ok(d_stride_k, esz) &&
-                   stride_ok(d_stride_j, esz);
+  const bool vec = logits_vec_ok(target_logits, draft_logits, esz, t_stride_b, t_stride_j,
+                                 d_stride_b, d_stride_k, d_stride_j);
   auto* base = reinterpret_cast<char*>(workspace);
   auto* part = reinterpret_cast<RowPartial*>(base + L.off_part);
-  auto* ws_lnz = reinterpret_cast<double*>(base + L.off_lnz);
-  auto* cnt = reinterpret_cast<uint32_t*>(base + L.off_cnt);
+  auto* rank = reinterpret_cast<int32_t*>(base + L.off_rank);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const RowSet rs{target_logits, t_stride_b, t_stride_j, draft_logits, d_stride_b, d_stride_k,
+                  d_stride_j, B, gamma + 1, K, gamma, temperature};
+  const int compact = B <= kMaxCompactB ? 1 : 0;
 
-  RowSet rs{target_logits, t_stride_b, t_stride_j, draft_logits, d_stride_b, d_stride_k,
-            d_stride_j, B, gamma + 1, K, gamma, temperature};
-  launch_rowstats(dtype, vec, rs, V, L, part, false, st);
+  StreamArgs sa{};
+  sa.rs = rs;
+  sa.V = V;
+  sa.compact = compact;
+  sa.part = part;
+  sa.rank_out = compact ? rank : nullptr;
+  const Partition p = launch_stream(dtype, vec, false, sa, L, st);
 
-  AcceptArgs aa{rs, V, L.nch, part, draft_tokens, seed, pos0, accept_len, out_token, logp, logq,
-                lnZ_target, lnZ_draft, device_error, ws_lnz, cnt};
-  if (dtype == SV_BF16)
-    hipLaunchKernelGGL(accept_kernel<SV_BF16>, dim3(unsigned(B)), dim3(kBlock), 0, st, aa);
-  else
-    hipLaunchKernelGGL(accept_kernel<SV_F32>, dim3(unsigned(B)), dim3(kBlock), 0, st, aa);
-
-  SampleArgs sa{target_logits, t_stride_b, t_stride_j, draft_logits, d_stride_b, d_stride_k,
-                d_stride_j, B, K, gamma, V, temperature, ws_lnz, ws_lnz + B * (gamma + 1),
-                nullptr, accept_len, seed, pos0, out_token, L.nsplit,
-                reinterpret_cast<Top2*>(base + L.off_top), cnt};
-  launch_sample(dtype, vec, sa, st);
+  ChainArgs ca{};
+  ca.rs = rs;
+  ca.V = V;
+  ca.p = p;
+  ca.compact = compact;
+  ca.part = part;
+  ca.rank = rank;
+  ca.tokens = draft_tokens;
+  ca.seed = seed;
+  ca.pos0 = pos0;
+  ca.accept_len = accept_len;
+  ca.out_token = out_token;
+  ca.logp = logp;
+  ca.logq = logq;
+  ca.lnz_t_out = lnZ_target;
+  ca.lnz_d_out = lnZ_draft;
+  ca.dev_err = device_error;
+  ca.nsplit = L.nsplit;
+  ca.cand = reinterpret_cast<Cand*>(base + L.off_top);
+  ca.info = reinterpret_cast<ChainInfo*>(base + L.off_info);
+  launch_chain(dtype, vec, ca, false, st);
   return launch_status();
 }
 
@@ -925,6 +1396,6 @@ const char* specverify_status_string(int status) {
   }
 }
 
-int specverify_version(void) { return 100; }
+int specverify_version(void) { return 200; }
 
 }  // extern "C"
