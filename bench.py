@@ -14,8 +14,10 @@ sample as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +32,7 @@ import workloads  # noqa: E402
 
 METRIC = "verified draft tokens/s + HBM GB/s (% of peak) at B=64, γ=8, V=128256 bf16"
 HBM_PEAK_GBPS = 8000.0
+COPY_BYTES = 1 << 28
 
 
 def algorithmic_bytes(w) -> int:
@@ -39,6 +42,27 @@ def algorithmic_bytes(w) -> int:
     logits = w.B * (w.gamma + 1) * w.V * e + sampled * w.K * w.gamma * w.V * e
     scalars = w.B * w.K * w.gamma * 4 + w.B * 4 + w.B * 8 + 2 * w.B * w.K * 4
     return logits + scalars
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "stream_kernel_B64_rows17_V128256_bf16_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "device_draft_verification_specverify_amd", "csrc",
+                             "specverify.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the streaming kernel from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when they
+    were taken on another version of the kernel source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            fields = dict(re.findall(r"^- (\w+): (\S+)\s*$", f.read(), re.M))
+        with open(KERNEL_SOURCE, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("source_sha256") != digest or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def stacked_inputs(w, dev):
@@ -73,6 +97,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=4,
                     help="input copies cycled so consecutive steps never reuse cached logits")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"after timing, copy {COPY_BYTES} bytes three times (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the verification path runs on a single device "
@@ -106,19 +132,26 @@ def main() -> int:
 
     # Dominant kernel: the streaming normaliser over the same 1088 rows, timed with
     # HIP events on the launch stream (the normalise entry point launches it plus a
-    # one-thread-per-row finalise).
+    # one-wavefront-per-row finalise).
     ws = sv.workspace(w.B, 0, 2 * w.gamma, w.V, sv.SV_BF16, dev)
-    temp_rows = temp
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     for i in range(args.warmup):
-        sv.specverify_normalize(copies[i % len(copies)][0], temp_rows, ws=ws)
+        sv.specverify_normalize(copies[i % len(copies)][0], temp, ws=ws)
     for i in range(args.steps):
         ev[i][0].record(stream)
-        sv.specverify_normalize(copies[i % len(copies)][0], temp_rows, ws=ws)
+        sv.specverify_normalize(copies[i % len(copies)][0], temp, ws=ws)
         ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    if args.copy_calibration:
+        # A plain device copy of known size, for scaling the HBM byte counters.
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
 
     out = plans[0].out
     err = int(out.device_error.item())
@@ -151,7 +184,7 @@ def main() -> int:
         "device_error": err,
         "roofline": {"bound": "hbm", "kernel": "stream_kernel (+finalize_rows_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
                      "bytes_per_launch": kernel_bytes, "avg_launch_ms": kern_ms},
     }
     if not args.no_cpu:

@@ -746,17 +746,21 @@ __device__ double rescore(const void* row_t, const void* row_d, bool residual, i
   return lp + log(-expm1(dd)) + g;
 }
 
-// Scan vectors vi0 + kBlock*it (it < kSampleIters) of the row pair: the loads of
-// all iterations are issued before any is scored.
+// Scan one split of the row pair. Each wavefront takes a contiguous quarter of
+// the split and lane l reads vectors vi0 + kWave*it (it < kSampleIters), so
+// the loads of a lane share one address and differ by immediate offsets; all
+// of them are issued before any is scored.
 template <int DT, bool VEC, bool RESIDUAL>
-__device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d, int64_t vi0,
+__device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d, int64_t split,
                                            int64_t V, const DrawParams& dp) {
   const int64_t vpr = (V + kVec - 1) / kVec;
   const bool partial_tail = (V % kVec) != 0;
+  const int64_t vi0 = split * (kSplit / kVec) +
+                      int64_t(threadIdx.x / kWave) * (kWave * kSampleIters) + (threadIdx.x & (kWave - 1));
   RawVec<DT> rt[kSampleIters], rd[kSampleIters];
 #pragma unroll
   for (int it = 0; it < kSampleIters; ++it) {
-    const int64_t vi = vi0 + int64_t(kBlock) * it;
+    const int64_t vi = vi0 + int64_t(kWave) * it;
     const bool inside = vi < vpr;
     rt[it] = inside ? load_vec_bounded<DT, VEC>(row_t, vi, V) : neg_inf_vec<DT>();
     if constexpr (RESIDUAL) rd[it] = inside ? load_vec_bounded<DT, VEC>(row_d, vi, V) : rt[it];
@@ -764,7 +768,7 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
   Top2 best = top2_empty();
 #pragma unroll
   for (int it = 0; it < kSampleIters; ++it) {
-    const int64_t vi = vi0 + int64_t(kBlock) * it;
+    const int64_t vi = vi0 + int64_t(kWave) * it;
     if (vi < vpr) {
       if (partial_tail && vi == vpr - 1)
         score_vec<DT, RESIDUAL, true>(rt[it], RESIDUAL ? rd[it] : rt[it], vi, V, dp, best);
@@ -960,9 +964,8 @@ void chain_kernel(ChainArgs a) {
   dp.r = uint32_t(chain);
   dp.s0 = uint32_t(a.seed);
   dp.s1 = uint32_t(a.seed >> 32);
-  const int64_t vi0 = split * (kSplit / kVec) + t;
-  Top2 best = residual ? scan_split<DT, VEC, true>(row_t, row_d, vi0, a.V, dp)
-                       : scan_split<DT, VEC, false>(row_t, row_d, vi0, a.V, dp);
+  Top2 best = residual ? scan_split<DT, VEC, true>(row_t, row_d, split, a.V, dp)
+                       : scan_split<DT, VEC, false>(row_t, row_d, split, a.V, dp);
   best = wave_top2(best);
   if (lane == 0) s_top[t / kWave] = best;
   __syncthreads();

@@ -54,7 +54,7 @@ def test_workspace_sizes():
 def _step(lib, **over):
     a = dict(t=8, d=8, dtype=1, tok=8, B=2, K=1, g=4, V=1000, tsb=5000, tsj=1000, dsb=4000, dsk=4000,
              dsj=1000, T=8, seed=1, pos0=None, n=8, y=8, lp=None, lq=None, zt=None, zd=None,
-             err=None, ws=256, wsb=1 << 20, st=None)
+             err=None, ws=256, wsb=1 << 24, st=None)
     a.update(over)
     order = ["t", "d", "dtype", "tok", "B", "K", "g", "V", "tsb", "tsj", "dsb", "dsk", "dsj", "T",
              "seed", "pos0", "n", "y", "lp", "lq", "zt", "zd", "err", "ws", "wsb", "st"]
@@ -90,7 +90,7 @@ def test_other_entry_points_validate_on_the_host():
     assert lib.specverify_accept(8, 8, 2, 1, 33, 0, None, 8, None, None) == -1
     assert lib.specverify_accept(8, 8, 0, 1, 4, 0, None, 8, None, None) == -1
     args = [8, 8, 1, 2, 1, 4, 1000, 5000, 1000, 4000, 4000, 1000, 8, 8, 8, 8, 8, 1, None, 8, 256,
-            1 << 20, None]
+            1 << 24, None]
     bad = list(args)
     bad[15] = None                                  # accept_len
     assert lib.specverify_residual_sample(*bad) == -1

@@ -208,3 +208,50 @@ def test_residual_entry_point_at_every_accept_length():
         torch.cuda.synchronize()
         got = out.cpu().numpy()
         assert np.array_equal(got[~flag], tok[~flag]), (n, got.ravel(), tok.ravel())
+
+
+@pytest.mark.parametrize("B,K,gamma,V,dtype", [
+    (16400, 1, 1, 40, "f32"),     # past the sampled-row table: draft rows of every batch row streamed
+    (13200, 5, 1, 24, "bf16"),    # 66000 chains
+])
+def test_large_batches(B, K, gamma, V, dtype):
+    print(f"[case] large batch B={B} K={K} gamma={gamma} V={V} {dtype}", flush=True)
+    w = workloads.make("c3", B=B, V=V, gamma=gamma, K=K, dtype=dtype,
+                       temps=("choice", (0.0, 0.5, 1.0)))
+    gpu = step_on_gpu(w)
+    rows = np.concatenate([np.arange(20), np.random.default_rng(5).choice(np.arange(20, B), 40,
+                                                                          replace=False)])
+    _report("large batch", compare_step(gpu, _ref(w, rows), w.temperature, rows))
+    assert int(gpu["device_error"][0]) == 0
+
+
+def test_workspace_reused_across_shapes_and_calls():
+    """One workspace serves calls of different sizes and repeated calls."""
+    shapes = [dict(B=8, V=5000, dtype="bf16"), dict(B=3, V=40000, dtype="f32", K=2),
+              dict(B=8, V=5000, dtype="bf16"), dict(B=33, V=777, gamma=3, dtype="f32")]
+    ws_bytes = max(sv.workspace_size(s["B"], s.get("K", 1), s.get("gamma", 8), s["V"],
+                                     sv.SV_BF16 if s["dtype"] == "bf16" else sv.SV_F32)
+                   for s in shapes)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=device())
+    for i, s in enumerate(shapes):
+        print(f"[case] shared workspace call {i}: {s}", flush=True)
+        w = workloads.make("c3", seed=i, temps=("choice", (0.0, 0.3, 1.0)), **s)
+        shared = step_on_gpu(w, ws=ws)
+        fresh = step_on_gpu(w)
+        for k, v in fresh.items():
+            if v is not None:
+                assert np.array_equal(v, shared[k], equal_nan=True), (i, k)
+        assert int(shared["device_error"][0]) == 0
+        _report(f"shared ws {i}", compare_step(shared, _ref(w), w.temperature))
+    # one plan called repeatedly on one stream
+    w = workloads.make("c3", B=16, V=9000)
+    plan = sv.StepPlan(logits_to_dev(w.target, w.dtype), logits_to_dev(w.draft, w.dtype),
+                       to_dev(w.tokens), to_dev(w.temperature), w.seed, to_dev(w.pos0))
+    first = None
+    for _ in range(6):
+        out = plan()
+        torch.cuda.synchronize()
+        cur = (out.accept_len.cpu().numpy().copy(), out.out_token.cpu().numpy().copy())
+        first = first or cur
+        assert np.array_equal(cur[0], first[0]) and np.array_equal(cur[1], first[1])
+    assert int(plan.out.device_error.item()) == 0
