@@ -109,7 +109,7 @@ def workspace(B: int, K: int, gamma: int, V: int, dtype: int, device) -> torch.T
     n = workspace_size(B, K, gamma, V, dtype)
     if n == 0:
         raise SpecVerifyError("sizes rejected by specverify_workspace_size")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)  # zero before first use
 
 
 def specverify_normalize(logits: torch.Tensor, temperature: torch.Tensor, want_argmax: bool = False,

@@ -45,10 +45,8 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kVec = 8;                    // logits per vector (16 B of bf16, 32 B of f32)
-constexpr int kUnroll = 4;                 // vectors in flight per lane in the stream loop
 constexpr int kSampleIters = 4;            // vectors per thread per sampling split
 constexpr int64_t kSplit = int64_t(kBlock) * kVec * kSampleIters;  // 8192 ids per split
-constexpr int64_t kMaxWaves = 16384;       // cap on stream wavefronts (sizes the workspace)
 constexpr int64_t kMaxCompactB = 16384;    // batch rows whose greedy drafts are compacted out
 constexpr int kMaxRowsPerChain = SV_MAX_GAMMA + 1 + SV_MAX_GAMMA;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -68,12 +66,15 @@ struct alignas(16) RowPartial {
   double s;
 };
 
-// Best two sampling candidates of one split, ordered by (key, id).
-struct alignas(16) Top2 {
+// Best two sampling candidates of one split, ordered by (key, id), with the
+// target and draft logits at each (so the float64 re-score reads no memory).
+struct Top2 {
   float k1;
   int32_t i1;
+  float t1, d1;
   float k2;
   int32_t i2;
+  float t2, d2;
 };
 
 // A split's draw result: the float64 score ln w_v + G_v of its best candidate.
@@ -247,74 +248,89 @@ struct RowSet {
   const float* temp;
 };
 
-struct Partition {
-  int64_t vpr;     // vectors per row
-  int64_t nrows;   // rows in the flattened space
-  int64_t N;       // vectors in the flattened space
-  int64_t W;       // stream wavefronts
-  int64_t maxseg;  // partial slots per wavefront
-};
+// Stream chunks: every stream row is cut into chunks of kWave * chunk_lanes(DT)
+// vectors (8 KB), one partial per chunk, stored row-major: part[rho * cpr + j].
+template <int DT>
+constexpr int chunk_lanes() { return DT == SV_BF16 ? 8 : 4; }  // vectors per lane per chunk
+inline int64_t chunk_vectors(int dtype) { return int64_t(kWave) * (dtype == SV_BF16 ? 8 : 4); }
 
-__device__ __forceinline__ int64_t range_lo(const Partition& p, int64_t w) {
-  return (w * p.N) / p.W;
-}
-// The wavefront whose range holds flattened vector `pos`.
-__device__ __forceinline__ int64_t wave_of(const Partition& p, int64_t pos) {
-  return ((pos + 1) * p.W - 1) / p.N;
-}
-
-// Merge the stream partials of flattened row rho in wavefront order. Waves
-// w0..w1 hold the row's first and last vector; when the stream has fewer
-// vectors than wavefronts some waves in between have empty ranges and wrote
-// nothing, so they are skipped.
 struct RowStat {
   double lnz;
   float m;
   int32_t idx;
 };
 
-template <int NB = 8>
-__device__ RowStat merge_row(const RowPartial* __restrict__ part, const Partition& p, int64_t rho,
-                             float T) {
-  const int64_t first = rho * p.vpr;
-  const int64_t w0 = wave_of(p, first);
-  const int64_t w1 = wave_of(p, first + p.vpr - 1);
-  float m = -INFINITY;
-  int32_t idx = INT_MAX;
-  double s = 0.0;
-  const double k2 = double(kLog2e / T);
-  // Partials are fetched NB at a time so their latencies overlap; each batch is
-  // folded into (m, s) with s rescaled when the maximum grows (exponents exact
-  // in double). The fold order is fixed, so the result is deterministic.
-  for (int64_t w = w0; w <= w1; w += NB) {
-    RowPartial buf[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int64_t ww = w + i;
-      const int64_t lo = range_lo(p, ww);
-      buf[i] = RowPartial{-INFINITY, INT_MAX, 0.0};
-      if (ww <= w1 && lo < range_lo(p, ww + 1)) buf[i] = part[ww * p.maxseg + (rho - lo / p.vpr)];
-    }
-    float bm = m;
-    int32_t bi = idx;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) better_max(bm, bi, buf[i].m, buf[i].idx);
-    if (T > 0.0f && bm > -INFINITY) {
-      if (m > -INFINITY) s *= exp2((double(m) - double(bm)) * k2);
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (buf[i].m != -INFINITY) s += buf[i].s * exp2((double(buf[i].m) - double(bm)) * k2);
-    }
-    m = bm;
-    idx = bi;
+// 2^e for a rescaling exponent e <= 0 between partial sums, in single
+// precision: about 1e-7 relative per term, far inside the normaliser tolerance.
+__device__ __forceinline__ double exp2_scale(double e) {
+  return double(__builtin_amdgcn_exp2f(float(e)));
+}
+
+// Fold chunk partial q into a lane's running (m, idx, s); s stays relative to
+// m in units of k2 = float(log2(e) / T).
+__device__ __forceinline__ void fold_partial(float& m, int32_t& idx, double& s, const RowPartial& q,
+                                             bool sampled, double k2) {
+  float bm = m;
+  int32_t bi = idx;
+  better_max(bm, bi, q.m, q.idx);
+  if (sampled && bm > -INFINITY) {
+    if (m > -INFINITY) s *= exp2_scale((double(m) - double(bm)) * k2);
+    if (q.m != -INFINITY) s += q.s * exp2_scale((double(q.m) - double(bm)) * k2);
   }
-  RowStat r;
-  r.m = m;
-  r.idx = idx;
-  if (T > 0.0f) r.lnz = (m > -INFINITY) ? double(m) / double(T) + log(s) : double(m);
-  else if (T == 0.0f) r.lnz = double(m);
-  else r.lnz = NAN;
-  return r;
+  m = bm;
+  idx = bi;
+}
+
+// Statistics of NR stream rows (rho[r] < 0: none) by one wavefront: lane l
+// folds chunks l, l + 64, ... of each row, the loads of all NR rows issued
+// together; then the lanes combine in a fixed order. Every lane returns the
+// result. lnZ: ln sum exp(z / T) for T > 0, the raw maximum for T == 0, NaN
+// otherwise (an all -inf row gives -inf).
+template <int NR>
+__device__ void wave_rows(const RowPartial* __restrict__ part, const int64_t (&rho)[NR],
+                          int64_t cpr, float T, RowStat (&out)[NR]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool sampled = T > 0.0f;
+  const double k2 = double(kLog2e / T);
+  float m[NR];
+  int32_t idx[NR];
+  double s[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    m[r] = -INFINITY;
+    idx[r] = INT_MAX;
+    s[r] = 0.0;
+  }
+  for (int64_t c = lane; c < cpr; c += kWave) {
+    RowPartial q[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      q[r] = rho[r] >= 0 ? part[rho[r] * cpr + c] : RowPartial{-INFINITY, INT_MAX, 0.0};
+#pragma unroll
+    for (int r = 0; r < NR; ++r) fold_partial(m[r], idx[r], s[r], q[r], sampled, k2);
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    float M = m[r];
+    int32_t I = idx[r];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const float om = __shfl_xor(M, off, kWave);
+      const int32_t oi = __shfl_xor(I, off, kWave);
+      better_max(M, I, om, oi);
+    }
+    double sr = 0.0;
+    if (sampled && M > -INFINITY) {
+      sr = m[r] > -INFINITY ? s[r] * exp2_scale((double(m[r]) - double(M)) * k2) : 0.0;
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
+    }
+    out[r].m = M;
+    out[r].idx = I;
+    if (sampled) out[r].lnz = M > -INFINITY ? double(M) / double(T) + log(sr) : double(M);
+    else if (T == 0.0f) out[r].lnz = double(M);
+    else out[r].lnz = NAN;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -367,166 +383,33 @@ __device__ int64_t select_sampled(const SampledTable& tab, int nchunks, int64_t 
 
 struct StreamArgs {
   RowSet rs;
-  int64_t V;
-  Partition p;           // in compact mode nrows and N are recomputed on the device
+  int64_t V, vpr;
+  int64_t cpr;           // chunks per row
+  int64_t nrows;         // stream rows (recomputed on the device in compact mode)
   int compact;
-  RowPartial* part;      // [W][maxseg]
+  RowPartial* part;      // [B*(P+K*G)][cpr]: slot b*P+j, then B*P + (b*K+k)*G+j
   int32_t* rank_out;     // [B + 1]: sampled batch rows before b; [B] = their total
 };
 
-// Online statistics of one lane over the vectors it reads in one row segment.
-// Sampled rows: running raw maximum m, c = float(m * k2) and s = sum of
-// 2^(z*k2 - c) (one fma + one exp per logit); greedy rows: maximum and lowest
-// argmax only. ARGMAX also tracks the argmax of sampled rows.
-template <int DT, bool SAMPLED, bool ARGMAX>
-struct LaneStats {
-  float m = -INFINITY;
-  float c = 0.0f;
-  double s = 0.0;
-  float am = -INFINITY;
-  int32_t idx = INT_MAX;
-  float k2 = 0.0f;
-
-  __device__ __forceinline__ void add(const RawVec<DT>* r, int n, int64_t vi0, int64_t vstride) {
-    if constexpr (SAMPLED) {
-      float lm = -INFINITY;
-      for (int u = 0; u < n; ++u)
-#pragma unroll
-        for (int t = 0; t < kVec; ++t) lm = fmaxf(lm, vec_elem<DT>(r[u], t));
-      if constexpr (ARGMAX) track(r, n, vi0, vstride);
-      if (lm > m) {
-        // s is 0 while m = -inf; scaling it there could compute 0 * inf
-        const float cn = lm * k2;
-        if (m != -INFINITY) s *= double(__builtin_amdgcn_exp2f(c - cn));
-        c = cn;
-        m = lm;
-      }
-      float acc = 0.0f;
-      for (int u = 0; u < n; ++u) {
-        float sv = 0.0f;
-#pragma unroll
-        for (int t = 0; t < kVec; ++t) sv += __builtin_amdgcn_exp2f(fmaf(vec_elem<DT>(r[u], t), k2, -c));
-        acc += sv;
-      }
-      s += double(acc);
-    } else {
-      track(r, n, vi0, vstride);
-    }
-  }
-
-  __device__ __forceinline__ void track(const RawVec<DT>* r, int n, int64_t vi0, int64_t vstride) {
-    for (int u = 0; u < n; ++u)
-#pragma unroll
-      for (int t = 0; t < kVec; ++t) {
-        const float x = vec_elem<DT>(r[u], t);
-        if (x > am) {
-          am = x;
-          idx = int32_t((vi0 + vstride * u) * kVec + t);
-        }
-      }
-  }
-};
-
-template <int DT, bool VEC>
-__device__ __forceinline__ void load_group(const void* row, int64_t vi0, RawVec<DT> (&r)[kUnroll]) {
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) r[u] = load_vec<DT, VEC, true>(row, vi0 + int64_t(kWave) * u);
-}
-
-// Vectors [v0, v1) of one row: lane l reads v0 + l + 64*i. Full groups of
-// 64*kUnroll vectors run without bounds checks, the next group's loads issued
-// before the current group is reduced; the last partial group is masked.
-template <int DT, bool VEC, bool SAMPLED, bool ARGMAX>
-__device__ __forceinline__ void scan_segment(const void* row, int64_t v0, int64_t v1, int lane,
-                                             LaneStats<DT, SAMPLED, ARGMAX>& st) {
-  constexpr int64_t step = int64_t(kWave) * kUnroll;
-  const int64_t nfull = (v1 - v0) / step;
-  int64_t base = v0;
-  if (nfull > 0) {
-    RawVec<DT> ra[kUnroll], rb[kUnroll];
-    load_group<DT, VEC>(row, base + lane, ra);
-    int64_t it = 0;
-    for (; it + 2 <= nfull; it += 2) {
-      load_group<DT, VEC>(row, base + step + lane, rb);
-      st.add(ra, kUnroll, base + lane, kWave);
-      if (it + 2 < nfull) load_group<DT, VEC>(row, base + 2 * step + lane, ra);
-      st.add(rb, kUnroll, base + step + lane, kWave);
-      base += 2 * step;
-    }
-    if (it < nfull) {
-      st.add(ra, kUnroll, base + lane, kWave);
-      base += step;
-    }
-  }
-  if (base < v1) {
-    RawVec<DT> r[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t vi = base + lane + int64_t(kWave) * u;
-      r[u] = vi < v1 ? load_vec<DT, VEC, true>(row, vi) : neg_inf_vec<DT>();
-    }
-    st.add(r, kUnroll, base + lane, kWave);
-  }
-}
-
-// Finish one row segment: lane 0 adds the row's partial last vector if the
-// segment holds it, then the wavefront reduces to one partial (fixed order).
-template <int DT, bool VEC, bool SAMPLED, bool ARGMAX>
-__device__ __forceinline__ RowPartial finish_segment(const void* row, bool tail, int64_t vtail,
-                                                     int64_t V, int lane,
-                                                     LaneStats<DT, SAMPLED, ARGMAX>& st) {
-  if (tail && lane == 0) {
-    const RawVec<DT> rv = load_vec_bounded<DT, VEC>(row, vtail, V);
-    st.add(&rv, 1, vtail, 0);
-  }
-  if constexpr (SAMPLED) {
-    // s = sum 2^(z*k2 - c); bring every lane to the wavefront maximum M:
-    // 2^((z - M) * k2) = 2^(z*k2 - c) * 2^(c - M*k2), exponent exact in double.
-    float M = st.m;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
-    double s = st.m != -INFINITY ? st.s * exp2(double(st.c) - double(M) * double(st.k2)) : 0.0;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
-    int32_t idx = st.idx;
-    if constexpr (ARGMAX) {
-      float am = st.am;
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        const float om = __shfl_xor(am, off, kWave);
-        const int32_t oi = __shfl_xor(idx, off, kWave);
-        better_max(am, idx, om, oi);
-      }
-    }
-    return RowPartial{M, idx, s};
-  } else {
-    float am = st.am;
-    int32_t idx = st.idx;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const float om = __shfl_xor(am, off, kWave);
-      const int32_t oi = __shfl_xor(idx, off, kWave);
-      better_max(am, idx, om, oi);
-    }
-    return RowPartial{am, idx, 0.0};
-  }
-}
-
-// One wavefront's contiguous range of the flattened stream.
+// Persistent wavefronts walk the chunks of the flattened stream round robin
+// (wavefront w takes chunks w, w + W, w + 2W, ...), so at any moment the grid
+// reads one moving window of the rows. A chunk's loads are all issued before
+// any is used. Sampled rows: chunk maximum M and s = sum 2^((z - M) * k2);
+// greedy rows: maximum and lowest argmax; ARGMAX_ALL: argmax of sampled rows too.
 template <int DT, bool VEC, bool ARGMAX_ALL>
 __global__ __launch_bounds__(kBlock) void stream_kernel(StreamArgs a) {
   __shared__ SampledTable tab;
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  constexpr int CL = chunk_lanes<DT>();
   const RowSet& rs = a.rs;
   const int lane = threadIdx.x & (kWave - 1);
-  Partition p = a.p;
   const int64_t BP = rs.B * rs.P;
   const int64_t KG = rs.K * rs.G;
   const int nchunks = int((rs.B + 63) / 64);
+  int64_t nrows = a.nrows;
   if (a.compact) {
     build_sampled_table(rs.temp, rs.B, tab);
-    p.nrows = BP + int64_t(tab.pref[nchunks]) * KG;
-    p.N = p.nrows * p.vpr;
+    nrows = BP + int64_t(tab.pref[nchunks]) * KG;
     if (blockIdx.x == 0 && a.rank_out) {
       for (int64_t b = threadIdx.x; b < rs.B; b += kBlock) {
         const int c = int(b >> 6);
@@ -535,19 +418,17 @@ __global__ __launch_bounds__(kBlock) void stream_kernel(StreamArgs a) {
       if (threadIdx.x == 0) a.rank_out[rs.B] = tab.pref[nchunks];
     }
   }
-  const int64_t w = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-  if (w >= p.W) return;
-  const int64_t hi = range_lo(p, w + 1);
-  int64_t pos = range_lo(p, w);
-  int seg = 0;
+  const int64_t cv = int64_t(kWave) * CL;
+  const int64_t total = nrows * a.cpr;
+  const int64_t W = int64_t(gridDim.x) * kWavesPerBlock;
   const bool v_tail = (a.V % kVec) != 0;
-  while (pos < hi) {
-    const int64_t rho = pos / p.vpr;
-    const int64_t rstart = rho * p.vpr;
-    const int64_t seg_end = hi < rstart + p.vpr ? hi : rstart + p.vpr;
-    // locate the row
+  for (int64_t c = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6); c < total; c += W) {
+    const int64_t rho = c / a.cpr;
+    const int64_t v0 = (c - rho * a.cpr) * cv;
+    const int64_t v1 = v0 + cv < a.vpr ? v0 + cv : a.vpr;
     const void* row;
     int64_t b;
+    int64_t slot = rho;  // partials sit by batch row: target rows, then draft rows (b, k, j)
     bool is_draft;
     if (rho < BP) {
       b = rho / rs.P;
@@ -563,87 +444,130 @@ __global__ __launch_bounds__(kBlock) void stream_kernel(StreamArgs a) {
       const int64_t j = rem - k * rs.G;
       row = row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj);
       is_draft = true;
+      slot = BP + b * KG + rem;
     }
-    const float T = rs.temp[b];
-    const bool sampled = T > 0.0f;
+    // In compact mode every streamed draft row belongs to a sampled batch row,
+    // so the chunk's loads go out before the temperature arrives; otherwise a
+    // greedy row's draft logits are skipped, never read.
+    const bool skip = is_draft && !a.compact && !(rs.temp[b] > 0.0f);
     RowPartial out{-INFINITY, INT_MAX, 0.0};
-    if (!(is_draft && !sampled)) {
-      const int64_t v0 = pos - rstart;
-      int64_t v1 = seg_end - rstart;
-      // the partial last vector of a row (V % 8 != 0) is added by lane 0 at the end
-      const bool tail = v_tail && v1 == p.vpr;
-      if (tail) v1 -= 1;
+    if (!skip) {
+      RawVec<DT> r[CL];
+#pragma unroll
+      for (int u = 0; u < CL; ++u) {
+        const int64_t vi = v0 + lane + int64_t(kWave) * u;
+        if (vi >= v1) r[u] = neg_inf_vec<DT>();
+        else if (v_tail && vi == a.vpr - 1) r[u] = load_vec_bounded<DT, VEC>(row, vi, a.V);
+        else r[u] = load_vec<DT, VEC, true>(row, vi);
+      }
+      const float T = rs.temp[b];
+      const bool sampled = T > 0.0f;
+      float am = -INFINITY;
+      int32_t ai = INT_MAX;
+      if (!sampled || ARGMAX_ALL) {
+#pragma unroll
+        for (int u = 0; u < CL; ++u)
+#pragma unroll
+          for (int q = 0; q < kVec; ++q) {
+            const float x = vec_elem<DT>(r[u], q);
+            if (x > am) {
+              am = x;
+              ai = int32_t((v0 + lane + int64_t(kWave) * u) * kVec + q);
+            }
+          }
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) {
+          const float om = __shfl_xor(am, off, kWave);
+          const int32_t oi = __shfl_xor(ai, off, kWave);
+          better_max(am, ai, om, oi);
+        }
+      }
       if (sampled) {
-        LaneStats<DT, true, ARGMAX_ALL> st;
-        st.k2 = kLog2e / T;
-        scan_segment<DT, VEC>(row, v0, v1, lane, st);
-        out = finish_segment<DT, VEC>(row, tail, p.vpr - 1, a.V, lane, st);
+        const float k2 = kLog2e / T;
+        float m = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < CL; ++u)
+#pragma unroll
+          for (int q = 0; q < kVec; ++q) m = fmaxf(m, vec_elem<DT>(r[u], q));
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+        double sum = 0.0;
+        if (m != -INFINITY) {
+          // 2^(z*k2 - c) with c = float(m*k2); d = m*k2 - c exactly (fma), and
+          // 2^((z - m)*k2) = 2^(z*k2 - c) * 2^(-d) with |d| < 1e-4: 1 - d ln 2.
+          const float c = m * k2;
+          const float d = fmaf(m, k2, -c);
+#pragma unroll
+          for (int u = 0; u < CL; ++u) {
+            float sv = 0.0f;
+#pragma unroll
+            for (int q = 0; q < kVec; ++q)
+              sv += __builtin_amdgcn_exp2f(fmaf(vec_elem<DT>(r[u], q), k2, -c));
+            sum += double(sv);
+          }
+#pragma unroll
+          for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+          sum *= 1.0 - double(d) * 0.69314718055994530942;
+        }
+        out = RowPartial{m, ai, sum};
       } else {
-        // greedy row (or invalid temperature): maximum and lowest argmax only
-        LaneStats<DT, false, true> st;
-        scan_segment<DT, VEC>(row, v0, v1, lane, st);
-        out = finish_segment<DT, VEC>(row, tail, p.vpr - 1, a.V, lane, st);
+        out = RowPartial{am, ai, 0.0};
       }
     }
-    if (lane == 0) a.part[w * p.maxseg + seg] = out;
-    ++seg;
-    pos = seg_end;
+    if (lane == 0) a.part[slot * a.cpr + (c - rho * a.cpr)] = out;
   }
 }
 
-// ln Z and argmax of every row (specverify_normalize): one wavefront per row,
-// lane i folding the row's partials i, i+64, ... so their loads overlap.
+// ln Z and argmax of every row (specverify_normalize): one wavefront per row.
 __global__ __launch_bounds__(kBlock) void finalize_rows_kernel(const RowPartial* __restrict__ part,
-                                                               Partition p, int64_t P,
+                                                               int64_t nrows, int64_t cpr, int64_t P,
                                                                const float* __restrict__ temp,
                                                                double* __restrict__ lnz,
                                                                int32_t* __restrict__ amax) {
   const int64_t rho = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-  if (rho >= p.nrows) return;
-  const int lane = threadIdx.x & (kWave - 1);
-  const float T = temp[rho / P];
-  const int64_t first = rho * p.vpr;
-  const int64_t w0 = wave_of(p, first);
-  const int64_t w1 = wave_of(p, first + p.vpr - 1);
-  float m = -INFINITY;
-  int32_t idx = INT_MAX;
-  double s = 0.0;
-  const double k2 = double(kLog2e / T);
-  for (int64_t ww = w0 + lane; ww <= w1; ww += kWave) {
-    const int64_t lo = range_lo(p, ww);
-    if (!(lo < range_lo(p, ww + 1))) continue;
-    const RowPartial q = part[ww * p.maxseg + (rho - lo / p.vpr)];
-    float bm = m;
-    int32_t bi = idx;
-    better_max(bm, bi, q.m, q.idx);
-    if (T > 0.0f && bm > -INFINITY) {
-      if (m > -INFINITY) s *= exp2((double(m) - double(bm)) * k2);
-      if (q.m != -INFINITY) s += q.s * exp2((double(q.m) - double(bm)) * k2);
-    }
-    m = bm;
-    idx = bi;
+  if (rho >= nrows) return;
+  const int64_t rows[1] = {rho};
+  RowStat st[1];
+  wave_rows<1>(part, rows, cpr, temp[rho / P], st);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    lnz[rho] = st[0].lnz;
+    if (amax) amax[rho] = st[0].idx == INT_MAX ? 0 : st[0].idx;
   }
-  float M = m;
-  int32_t I = idx;
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const float om = __shfl_xor(M, off, kWave);
-    const int32_t oi = __shfl_xor(I, off, kWave);
-    better_max(M, I, om, oi);
-  }
-  if (T > 0.0f && M > -INFINITY) {
-    s = m > -INFINITY ? s * exp2((double(m) - double(M)) * k2) : 0.0;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
-  }
-  if (lane == 0) {
-    double r;
-    if (T > 0.0f) r = M > -INFINITY ? double(M) / double(T) + log(s) : double(M);
-    else if (T == 0.0f) r = double(M);
-    else r = NAN;
-    lnz[rho] = r;
-    if (amax) amax[rho] = I == INT_MAX ? 0 : I;
-  }
+}
+
+// ---------------------------------------------------------------------------
+// Hand-offs between workgroups of one launch: data are published with relaxed
+// agent-scope atomic stores, which gfx950 writes through to the device
+// coherence point, and read with relaxed agent-scope atomic loads; the
+// publisher waits for its stores to complete (vmcnt = 0) before the counter
+// bump that announces them, so no L2 write-back is needed.
+__device__ __forceinline__ void pub64(void* p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get64(const void* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void pub32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t get32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t bump32(uint32_t* p) {
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wavefront's earlier memory operations have completed.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void pub_cand(Cand* p, const Cand& c) {
+  pub64(p, uint64_t(__double_as_longlong(c.score)));
+  pub64(reinterpret_cast<char*>(p) + 8, uint64_t(uint32_t(c.id)));
+}
+__device__ __forceinline__ Cand get_cand(const Cand* p) {
+  const uint64_t a = get64(p);
+  const uint64_t b = get64(reinterpret_cast<const char*>(p) + 8);
+  return Cand{__longlong_as_double(int64_t(a)), int32_t(uint32_t(b)), 0};
 }
 
 // ---------------------------------------------------------------------------
@@ -653,34 +577,42 @@ __device__ __forceinline__ bool cand_less(float ka, int32_t ia, float kb, int32_
 
 // Insert a candidate whose id is larger than every id already held (the ids a
 // thread visits only grow), so ties keep the earlier, lower id; no branches.
-__device__ __forceinline__ void top2_push(Top2& s, float key, int32_t id) {
+__device__ __forceinline__ void top2_push(Top2& s, float key, int32_t id, float zt, float zd) {
   const bool b1 = key < s.k1;
   const bool b2 = key < s.k2;
   s.k2 = b1 ? s.k1 : (b2 ? key : s.k2);
   s.i2 = b1 ? s.i1 : (b2 ? id : s.i2);
+  s.t2 = b1 ? s.t1 : (b2 ? zt : s.t2);
+  s.d2 = b1 ? s.d1 : (b2 ? zd : s.d2);
   s.k1 = b1 ? key : s.k1;
   s.i1 = b1 ? id : s.i1;
+  s.t1 = b1 ? zt : s.t1;
+  s.d1 = b1 ? zd : s.d1;
 }
 
 __device__ __forceinline__ Top2 top2_merge(const Top2& a, const Top2& b) {
   Top2 r;
   if (cand_less(b.k1, b.i1, a.k1, a.i1)) {
-    r.k1 = b.k1;
-    r.i1 = b.i1;
+    r.k1 = b.k1; r.i1 = b.i1; r.t1 = b.t1; r.d1 = b.d1;
     const bool second_a = cand_less(a.k1, a.i1, b.k2, b.i2);
     r.k2 = second_a ? a.k1 : b.k2;
     r.i2 = second_a ? a.i1 : b.i2;
+    r.t2 = second_a ? a.t1 : b.t2;
+    r.d2 = second_a ? a.d1 : b.d2;
   } else {
-    r.k1 = a.k1;
-    r.i1 = a.i1;
+    r.k1 = a.k1; r.i1 = a.i1; r.t1 = a.t1; r.d1 = a.d1;
     const bool second_b = cand_less(b.k1, b.i1, a.k2, a.i2);
     r.k2 = second_b ? b.k1 : a.k2;
     r.i2 = second_b ? b.i1 : a.i2;
+    r.t2 = second_b ? b.t1 : a.t2;
+    r.d2 = second_b ? b.d1 : a.d2;
   }
   return r;
 }
 
-__device__ __forceinline__ Top2 top2_empty() { return Top2{INFINITY, INT_MAX, INFINITY, INT_MAX}; }
+__device__ __forceinline__ Top2 top2_empty() {
+  return Top2{INFINITY, INT_MAX, 0.0f, 0.0f, INFINITY, INT_MAX, 0.0f, 0.0f};
+}
 
 __device__ __forceinline__ Top2 wave_top2(Top2 v) {
 #pragma unroll
@@ -688,8 +620,12 @@ __device__ __forceinline__ Top2 wave_top2(Top2 v) {
     Top2 o;
     o.k1 = __shfl_xor(v.k1, off, kWave);
     o.i1 = __shfl_xor(v.i1, off, kWave);
+    o.t1 = __shfl_xor(v.t1, off, kWave);
+    o.d1 = __shfl_xor(v.d1, off, kWave);
     o.k2 = __shfl_xor(v.k2, off, kWave);
     o.i2 = __shfl_xor(v.i2, off, kWave);
+    o.t2 = __shfl_xor(v.t2, off, kWave);
+    o.d2 = __shfl_xor(v.d2, off, kWave);
     v = top2_merge(v, o);
   }
   return v;
@@ -725,25 +661,41 @@ __device__ __forceinline__ void score_vec(const RawVec<DT>& rt, const RawVec<DT>
     const float e2 = -__builtin_amdgcn_logf(unit_uniform(word));
     float key = (w > 0.0f) ? e2 * __builtin_amdgcn_rcpf(w) : INFINITY;
     if constexpr (PARTIAL) key = (vi * kVec + t < V) ? key : INFINITY;
-    top2_push(best, key, int32_t(vi * kVec + t));
+    top2_push(best, key, int32_t(vi * kVec + t), zt, RESIDUAL ? vec_elem<DT>(rd, t) : 0.0f);
   }
 }
 
-// float64 score of candidate v: ln w_v + G_v with G_v = -ln(-ln u_v).
-template <int DT>
-__device__ double rescore(const void* row_t, const void* row_d, bool residual, int32_t v, double T,
-                          double lzt, double lzd, uint32_t pos, uint32_t r, uint32_t s0,
-                          uint32_t s1) {
+// float64 score of candidate v with target / draft logits zt, zd:
+// ln w_v + G_v with G_v = -ln(-ln u_v).
+__device__ double rescore(bool residual, int32_t v, float zt, float zd, double T, double lzt,
+                          double lzd, uint32_t pos, uint32_t r, uint32_t s0, uint32_t s1) {
   if (v < 0 || v == INT_MAX) return -INFINITY;
   const Philox4 blk = philox4x32_10(uint32_t(v) >> 2, pos, r, kPurposeSample, s0, s1);
   const double u = unit_uniform_d(blk.w[v & 3]);
   const double g = -log(-log_uniform_d(u));
-  const double lp = double(load_one<DT>(row_t, v)) / T - lzt;
+  const double lp = double(zt) / T - lzt;
   if (!residual) return lp + g;
-  const double lq = double(load_one<DT>(row_d, v)) / T - lzd;
+  const double lq = double(zd) / T - lzd;
   const double dd = lq - lp;
   if (!(dd < 0.0)) return -INFINITY;
   return lp + log(-expm1(dd)) + g;
+}
+
+// Float64 re-score of a block's best two by lanes 0 and 1 of the calling
+// wavefront; lane 0 returns the winner (score -inf and id INT_MAX if none).
+__device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, double T, double lzt,
+                                             double lzd, uint32_t pos, uint32_t r, uint32_t s0,
+                                             uint32_t s1) {
+  const int lane = threadIdx.x & (kWave - 1);
+  double sc = -INFINITY;
+  if (lane < 2)
+    sc = lane == 0 ? rescore(residual, all.i1, all.t1, all.d1, T, lzt, lzd, pos, r, s0, s1)
+                   : rescore(residual, all.i2, all.t2, all.d2, T, lzt, lzd, pos, r, s0, s1);
+  const double sc2 = __shfl(sc, 1, kWave);
+  Cand c{sc, all.i1, 0};
+  if (sc2 > sc || (sc2 == sc && all.i2 < all.i1)) c = Cand{sc2, all.i2, 0};
+  if (c.score == -INFINITY) c.id = INT_MAX;
+  return c;
 }
 
 // Scan one split of the row pair. Each wavefront takes a contiguous quarter of
@@ -782,10 +734,8 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
 struct ChainArgs {
   RowSet rs;
   int64_t V;
-  Partition p;               // stream partition (compact mode: nrows/N taken from rank[B])
-  int compact;
-  const RowPartial* part;
-  const int32_t* rank;       // [B + 1] (compact mode)
+  const RowPartial* part;    // stream chunk partials by batch-row slot
+  int64_t cpr;               // chunks per row
   const int32_t* tokens;     // [B, K, G]
   uint64_t seed;
   const int64_t* pos0;
@@ -805,7 +755,8 @@ struct ChainArgs {
   // to the finish kernel
   int64_t nsplit;
   Cand* cand;                // [B*K][nsplit]
-  ChainInfo* info;           // [B*K]
+  ChainInfo* info;           // [B*K] (for finish_kernel)
+  uint32_t* cnt;             // [B*K] splits done per chain, or null: finish_kernel picks the token
 };
 
 // At least 4 waves per SIMD: a 256-thread workgroup per (chain, split) then
@@ -819,6 +770,7 @@ void chain_kernel(ChainArgs a) {
   __shared__ int32_t s_bad;
   __shared__ int32_t s_n;
   __shared__ Top2 s_top[kWavesPerBlock];
+  __shared__ uint32_t s_last;
   const RowSet& rs = a.rs;
   const int64_t chain = blockIdx.x / a.nsplit;
   const int64_t split = blockIdx.x - chain * a.nsplit;
@@ -846,11 +798,6 @@ void chain_kernel(ChainArgs a) {
     __syncthreads();
     if (greedy && lead && t == 0 && s_n >= 0) a.out_token[chain] = s_amax[s_n];
   } else {
-    Partition p = a.p;
-    if (a.compact) {
-      p.nrows = rs.B * P + int64_t(a.rank[rs.B]) * rs.K * G;
-      p.N = p.nrows * p.vpr;
-    }
     // Loads that do not depend on the normalisers go first so their latency
     // overlaps the merges: draft tokens, the logits at them, accept uniforms.
     int32_t x = 0;
@@ -870,28 +817,38 @@ void chain_kernel(ChainArgs a) {
       log_u = log_uniform_d(unit_uniform_d(r.w[0]));
     }
     if (t == 0) s_bad = 0;
+    if (t >= P && t < P + G) s_lnz[t] = NAN;  // stays NaN for a greedy row's drafts
     __syncthreads();
-    // normalisers of the chain's rows: target rows 0..G, then draft rows (k, 0..G-1)
-    if (t < P + G) {
-      const bool is_draft = t >= P;
-      double lnz = NAN;
-      if (!is_draft || sampled) {
-        int64_t rho;
-        if (!is_draft) {
-          rho = b * P + t;
-        } else {
-          const int64_t sb = a.compact ? int64_t(a.rank[b]) : b;
-          rho = rs.B * P + sb * rs.K * G + k * G + (t - P);
+    // normalisers of the chain's rows (target rows 0..G, then draft rows
+    // (k, 0..G-1) when sampled): wavefront w merges rows w, w + 4, ..., five
+    // at a time with all their partial loads issued together
+    {
+      const int nr = P + (sampled ? G : 0);
+      const int wv = t / kWave;
+      for (int base = wv; base < nr; base += 5 * kWavesPerBlock) {
+        int64_t rho[5];
+#pragma unroll
+        for (int r = 0; r < 5; ++r) {
+          const int ri = base + kWavesPerBlock * r;
+          rho[r] = ri >= nr ? -1 : ri < P ? b * P + ri : rs.B * P + chain * G + (ri - P);
         }
-        const RowStat r = merge_row<4>(a.part, p, rho, T);
-        lnz = r.lnz;
-        if (!(r.m > -INFINITY)) atomicOr(&s_bad, SV_ERR_ROW);
-        if (!is_draft) s_amax[t] = r.idx == INT_MAX ? 0 : r.idx;
-      }
-      s_lnz[t] = lnz;
-      if (lead) {
-        if (!is_draft && k == 0 && a.lnz_t_out) a.lnz_t_out[b * P + t] = lnz;
-        if (is_draft && sampled && a.lnz_d_out) a.lnz_d_out[chain * G + (t - P)] = lnz;
+        RowStat st[5];
+        wave_rows<5>(a.part, rho, a.cpr, T, st);
+        if (lane == 0) {
+#pragma unroll
+          for (int r = 0; r < 5; ++r) {
+            const int ri = base + kWavesPerBlock * r;
+            if (ri >= nr) continue;
+            s_lnz[ri] = st[r].lnz;
+            if (!(st[r].m > -INFINITY)) atomicOr(&s_bad, SV_ERR_ROW);
+            if (ri < P) {
+              s_amax[ri] = st[r].idx == INT_MAX ? 0 : st[r].idx;
+              if (lead && k == 0 && a.lnz_t_out) a.lnz_t_out[b * P + ri] = st[r].lnz;
+            } else if (lead && a.lnz_d_out) {
+              a.lnz_d_out[chain * G + (ri - P)] = st[r].lnz;
+            }
+          }
+        }
       }
     }
     __syncthreads();
@@ -972,19 +929,57 @@ void chain_kernel(ChainArgs a) {
   if (t < kWave) {
     Top2 all = s_top[0];
     for (int w = 1; w < kWavesPerBlock; ++w) all = top2_merge(all, s_top[w]);
-    // lanes 0 and 1 re-score the two candidates side by side
-    const int32_t id = lane == 0 ? all.i1 : all.i2;
-    double sc = -INFINITY;
-    if (lane < 2)
-      sc = rescore<DT>(row_t, row_d, residual, id, double(T), lzt, lzd, dp.pos, dp.r, dp.s0, dp.s1);
-    const double sc2 = __shfl(sc, 1, kWave);
+    const Cand c = rescore_top2(all, residual, double(T), lzt, lzd, dp.pos, dp.r, dp.s0, dp.s1);
     if (lane == 0) {
-      Cand c{sc, all.i1, 0};
-      if (sc2 > sc || (sc2 == sc && all.i2 < all.i1)) c = Cand{sc2, all.i2, 0};
-      if (c.score == -INFINITY) c.id = INT_MAX;
-      a.cand[chain * a.nsplit + split] = c;
+      if (!a.cnt) {
+        a.cand[chain * a.nsplit + split] = c;
+      } else {
+        pub_cand(a.cand + chain * a.nsplit + split, c);
+        stores_done();
+        const uint32_t prev = bump32(a.cnt + chain);
+        s_last = prev == uint32_t(a.nsplit - 1);
+        if (s_last) pub32(a.cnt + chain, 0u);  // every split is counted: zero for the next call
+      }
     }
   }
+  if (!a.cnt) return;
+  __syncthreads();
+  if (!s_last || t >= kWave) return;
+  // The chain's last split picks the token: the best float64 score over the
+  // splits (ties to the lowest id); no candidate anywhere means an empty
+  // residual support (rounding only), drawn from p_n with the same noise.
+  double bs = -INFINITY;
+  int32_t id = INT_MAX;
+  for (int64_t sp = lane; sp < a.nsplit; sp += kWave) {
+    const Cand q = get_cand(a.cand + chain * a.nsplit + sp);
+    if (q.score > bs || (q.score == bs && q.id < id)) {
+      bs = q.score;
+      id = q.id;
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const double ob = __shfl_xor(bs, off, kWave);
+    const int32_t oi = __shfl_xor(id, off, kWave);
+    if (ob > bs || (ob == bs && oi < id)) {
+      bs = ob;
+      id = oi;
+    }
+  }
+  if (id == INT_MAX) {
+    DrawParams fp = dp;
+    fp.D2 = 0.0f;
+    const int64_t vpr = (a.V + kVec - 1) / kVec;
+    Top2 fb = top2_empty();
+    for (int64_t vi = lane; vi < vpr; vi += kWave) {
+      const RawVec<DT> pt = load_vec_bounded<DT, VEC>(row_t, vi, a.V);
+      score_vec<DT, false, true>(pt, pt, vi, a.V, fp, fb);
+    }
+    fb = wave_top2(fb);
+    id = rescore_top2(fb, false, double(T), lzt, 0.0, fp.pos, fp.r, fp.s0, fp.s1).id;
+    id = __shfl(id, 0, kWave);
+  }
+  if (lane == 0) a.out_token[chain] = id == INT_MAX ? -1 : id;
 }
 
 // One wavefront per chain: the best float64 score over the splits wins (ties
@@ -1043,13 +1038,8 @@ __global__ __launch_bounds__(kWave) void finish_kernel(const void* tgt, int64_t 
       score_vec<DT, false, true>(pt, pt, vi, V, dp, fb);
     }
     fb = wave_top2(fb);
-    double sc = -INFINITY;
-    if (lane < 2)
-      sc = rescore<DT>(row_t, row_t, false, lane == 0 ? fb.i1 : fb.i2, double(T), ci.lzt, 0.0,
-                       dp.pos, dp.r, dp.s0, dp.s1);
-    const double sc2 = __shfl(sc, 1, kWave);
-    id = fb.i1;
-    if (sc2 > sc || (sc2 == sc && fb.i2 < fb.i1)) id = fb.i2;
+    id = rescore_top2(fb, false, double(T), ci.lzt, 0.0, dp.pos, dp.r, dp.s0, dp.s1).id;
+    id = __shfl(id, 0, kWave);
   }
   if (lane == 0) out_token[chain] = id == INT_MAX ? -1 : id;
 }
@@ -1085,41 +1075,37 @@ __global__ __launch_bounds__(kBlock) void accept_scalar_kernel(const float* __re
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  int64_t vpr, nrows, chains, nsplit, part_slots;
+  int64_t vpr, cpr, nrows, chains, nsplit;
   size_t off_part, off_rank, off_info, off_top, total;
 };
 
-// part_slots bounds W * maxseg for every W <= kMaxWaves: maxseg(W) <= N/(W*vpr) + 3.
-Layout make_layout(int64_t B, int64_t nrows, int64_t chains, int64_t V) {
+// Chain counters at the start of every workspace, at a fixed place whatever
+// the sizes: zero before a workspace's first use, and every completed call
+// leaves them zero. Steps with more chains pick their tokens in finish_kernel.
+constexpr int64_t kMaxCountedChains = 65536;
+constexpr size_t kCounterBytes = kMaxCountedChains * sizeof(uint32_t);
+
+// One chunk partial per (stream row, chunk); every row of the batch counted.
+Layout make_layout(int64_t B, int64_t nrows, int64_t chains, int64_t V, int dtype) {
   Layout L;
   L.vpr = (V + kVec - 1) / kVec;
+  const int64_t cv = chunk_vectors(dtype);
+  L.cpr = (L.vpr + cv - 1) / cv;
   L.nrows = nrows;
   L.chains = chains;
   L.nsplit = (V + kSplit - 1) / kSplit;
-  L.part_slots = nrows + 3 * kMaxWaves;
-  L.off_part = 0;
-  L.off_rank = align256(L.off_part + size_t(L.part_slots) * sizeof(RowPartial));
+  L.off_part = kCounterBytes;
+  L.off_rank = align256(L.off_part + size_t(nrows) * size_t(L.cpr) * sizeof(RowPartial));
   L.off_info = align256(L.off_rank + size_t(B + 1) * sizeof(int32_t));
   L.off_top = align256(L.off_info + size_t(chains) * sizeof(ChainInfo));
   L.total = align256(L.off_top + size_t(chains) * size_t(L.nsplit) * sizeof(Cand));
   return L;
 }
 
-Partition make_partition(const Layout& L, int64_t W) {
-  Partition p;
-  p.vpr = L.vpr;
-  p.nrows = L.nrows;
-  p.N = L.nrows * L.vpr;
-  p.W = W;
-  const int64_t range = (p.N + W - 1) / W;
-  p.maxseg = range / L.vpr + 2;
-  return p;
-}
-
-// Wavefronts of one stream-kernel instantiation that fit on the device at once
-// (cached per device; only balance depends on it, never correctness).
+// Workgroups of one stream-kernel instantiation resident on the device at
+// once: the persistent grid (cached per device; only speed depends on it).
 template <int DT, bool VEC, bool ARGMAX_ALL>
-int64_t stream_waves() {
+int64_t stream_blocks() {
   static std::atomic<int64_t> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
@@ -1136,11 +1122,9 @@ int64_t stream_waves() {
                                                    kBlock, 0) != hipSuccess ||
       blocks <= 0)
     blocks = 4;
-  int64_t w = int64_t(cus) * blocks * kWavesPerBlock;
-  if (w > kMaxWaves) w = kMaxWaves;
-  w -= w % kWavesPerBlock;
-  if (dev < 64) cache[dev].store(w, std::memory_order_relaxed);
-  return w;
+  const int64_t n = int64_t(cus) * blocks;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -1150,28 +1134,26 @@ int esize(int dtype) { return dtype == SV_BF16 ? 2 : 4; }
 int launch_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP; }
 
 template <int DT, bool VEC, bool ARGMAX_ALL>
-Partition launch_stream_t(StreamArgs sa, const Layout& L, hipStream_t st) {
-  const int64_t W = stream_waves<DT, VEC, ARGMAX_ALL>();
-  sa.p = make_partition(L, W);
-  hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(W / kWavesPerBlock)),
-                     dim3(kBlock), 0, st, sa);
-  return sa.p;
+void launch_stream_t(const StreamArgs& sa, hipStream_t st) {
+  int64_t grid = stream_blocks<DT, VEC, ARGMAX_ALL>();
+  const int64_t need = (sa.nrows * sa.cpr + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (grid > need) grid = need;
+  hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(grid)), dim3(kBlock), 0,
+                     st, sa);
 }
 
-// Returns the partition the merge kernels must use (in compact mode they
-// replace nrows and N by the counts the stream kernel wrote to rank[B]).
-Partition launch_stream(int dtype, bool vec, bool argmax_all, const StreamArgs& sa,
-                        const Layout& L, hipStream_t st) {
+void launch_stream(int dtype, bool vec, bool argmax_all, const StreamArgs& sa, hipStream_t st) {
   if (dtype == SV_BF16) {
-    if (vec) return argmax_all ? launch_stream_t<SV_BF16, true, true>(sa, L, st)
-                               : launch_stream_t<SV_BF16, true, false>(sa, L, st);
-    return argmax_all ? launch_stream_t<SV_BF16, false, true>(sa, L, st)
-                      : launch_stream_t<SV_BF16, false, false>(sa, L, st);
+    if (vec) argmax_all ? launch_stream_t<SV_BF16, true, true>(sa, st)
+                        : launch_stream_t<SV_BF16, true, false>(sa, st);
+    else argmax_all ? launch_stream_t<SV_BF16, false, true>(sa, st)
+                    : launch_stream_t<SV_BF16, false, false>(sa, st);
+    return;
   }
-  if (vec) return argmax_all ? launch_stream_t<SV_F32, true, true>(sa, L, st)
-                             : launch_stream_t<SV_F32, true, false>(sa, L, st);
-  return argmax_all ? launch_stream_t<SV_F32, false, true>(sa, L, st)
-                    : launch_stream_t<SV_F32, false, false>(sa, L, st);
+  if (vec) argmax_all ? launch_stream_t<SV_F32, true, true>(sa, st)
+                      : launch_stream_t<SV_F32, true, false>(sa, st);
+  else argmax_all ? launch_stream_t<SV_F32, false, true>(sa, st)
+                  : launch_stream_t<SV_F32, false, false>(sa, st);
 }
 
 template <int DT, bool VEC>
@@ -1180,6 +1162,7 @@ void launch_chain_finish(const ChainArgs& ca, bool given, hipStream_t st) {
   const dim3 grid{unsigned(chains * ca.nsplit), 1u, 1u};
   if (given) hipLaunchKernelGGL((chain_kernel<DT, VEC, true>), grid, dim3(kBlock), 0, st, ca);
   else hipLaunchKernelGGL((chain_kernel<DT, VEC, false>), grid, dim3(kBlock), 0, st, ca);
+  if (ca.cnt) return;  // the chains' last splits picked the tokens
   const RowSet& rs = ca.rs;
   hipLaunchKernelGGL((finish_kernel<DT, VEC>), dim3(unsigned(chains)), dim3(kWave), 0, st, rs.t,
                      rs.tsb, rs.tsj, rs.K, rs.G, ca.V, rs.temp, ca.seed, ca.pos0, ca.info,
@@ -1216,8 +1199,8 @@ bool workspace_ok(void* ws, size_t have, size_t need, int* status) {
   return true;
 }
 
-Layout step_layout(int64_t B, int64_t K, int64_t G, int64_t V) {
-  return make_layout(B, B * (G + 1) + B * K * G, B * K, V);
+Layout step_layout(int64_t B, int64_t K, int64_t G, int64_t V, int dtype) {
+  return make_layout(B, B * (G + 1) + B * K * G, B * K, V, dtype);
 }
 
 bool logits_vec_ok(const void* t, const void* d, int esz, int64_t tsb, int64_t tsj, int64_t dsb,
@@ -1236,10 +1219,10 @@ size_t specverify_workspace_size(int64_t B, int64_t K, int64_t gamma, int64_t V,
     if (B < 1 || gamma < 0 || V < 1 || V >= (int64_t(1) << 31) ||
         B > (int64_t(1) << 40) / (gamma + 1))
       return 0;
-    return make_layout(B, B * (gamma + 1), 0, V).total;
+    return make_layout(B, B * (gamma + 1), 0, V, dtype).total;
   }
   if (!sizes_ok(B, K, gamma, V)) return 0;
-  return step_layout(B, K, gamma, V).total;
+  return step_layout(B, K, gamma, V, dtype).total;
 }
 
 int specverify_normalize(const void* logits, int dtype, int64_t B, int64_t P, int64_t V,
@@ -1251,7 +1234,7 @@ int specverify_normalize(const void* logits, int dtype, int64_t B, int64_t P, in
       B > (int64_t(1) << 40) / P)
     return SV_EINVAL;
   if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
-  const Layout L = make_layout(B, B * P, 0, V);
+  const Layout L = make_layout(B, B * P, 0, V, dtype);
   int status = SV_OK;
   if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
   const int esz = esize(dtype);
@@ -1262,13 +1245,16 @@ int specverify_normalize(const void* logits, int dtype, int64_t B, int64_t P, in
   StreamArgs sa{};
   sa.rs = RowSet{logits, stride_b, stride_p, nullptr, 0, 0, 0, B, P, 0, 1, temperature};
   sa.V = V;
+  sa.vpr = L.vpr;
+  sa.cpr = L.cpr;
+  sa.nrows = B * P;
   sa.compact = 0;
   sa.part = part;
   sa.rank_out = nullptr;
-  const Partition p = launch_stream(dtype, vec, argmax != nullptr, sa, L, st);
+  launch_stream(dtype, vec, argmax != nullptr, sa, st);
   hipLaunchKernelGGL(finalize_rows_kernel,
                      dim3(unsigned((B * P + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kBlock), 0,
-                     st, part, p, P, temperature, lnZ, argmax);
+                     st, part, B * P, L.cpr, P, temperature, lnZ, argmax);
   return launch_status();
 }
 
@@ -1300,7 +1286,7 @@ int specverify_residual_sample(const void* target_logits, const void* draft_logi
   if (t_stride_b < 0 || t_stride_j < 0 || d_stride_b < 0 || d_stride_k < 0 || d_stride_j < 0)
     return SV_EINVAL;
   if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
-  const Layout L = step_layout(B, K, gamma, V);
+  const Layout L = step_layout(B, K, gamma, V, dtype);
   int status = SV_OK;
   if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
   const int esz = esize(dtype);
@@ -1322,6 +1308,7 @@ int specverify_residual_sample(const void* target_logits, const void* draft_logi
   ca.nsplit = L.nsplit;
   ca.cand = reinterpret_cast<Cand*>(base + L.off_top);
   ca.info = reinterpret_cast<ChainInfo*>(base + L.off_info);
+  ca.cnt = B * K <= kMaxCountedChains ? reinterpret_cast<uint32_t*>(base) : nullptr;
   launch_chain(dtype, vec, ca, true, st);
   return launch_status();
 }
@@ -1341,7 +1328,7 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
   if (t_stride_b < 0 || t_stride_j < 0 || d_stride_b < 0 || d_stride_k < 0 || d_stride_j < 0)
     return SV_EINVAL;
   if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
-  const Layout L = step_layout(B, K, gamma, V);
+  const Layout L = step_layout(B, K, gamma, V, dtype);
   int status = SV_OK;
   if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
   const int esz = esize(dtype);
@@ -1358,18 +1345,19 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
   StreamArgs sa{};
   sa.rs = rs;
   sa.V = V;
+  sa.vpr = L.vpr;
+  sa.cpr = L.cpr;
+  sa.nrows = L.nrows;
   sa.compact = compact;
   sa.part = part;
   sa.rank_out = compact ? rank : nullptr;
-  const Partition p = launch_stream(dtype, vec, false, sa, L, st);
+  launch_stream(dtype, vec, false, sa, st);
 
   ChainArgs ca{};
   ca.rs = rs;
   ca.V = V;
-  ca.p = p;
-  ca.compact = compact;
   ca.part = part;
-  ca.rank = rank;
+  ca.cpr = L.cpr;
   ca.tokens = draft_tokens;
   ca.seed = seed;
   ca.pos0 = pos0;
@@ -1383,6 +1371,7 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
   ca.nsplit = L.nsplit;
   ca.cand = reinterpret_cast<Cand*>(base + L.off_top);
   ca.info = reinterpret_cast<ChainInfo*>(base + L.off_info);
+  ca.cnt = B * K <= kMaxCountedChains ? reinterpret_cast<uint32_t*>(base) : nullptr;
   launch_chain(dtype, vec, ca, false, st);
   return launch_status();
 }

@@ -42,9 +42,12 @@
  * - Results are bit-deterministic: reductions merge in a fixed order and no
  *   floating-point atomics are used.
  * - `workspace` is device scratch of at least specverify_workspace_size()
- *   bytes, 256-byte aligned. It needs no initialisation and its contents are
- *   undefined between calls; one buffer serves any number of calls ordered
- *   on one stream, and calls that overlap in time on one buffer race.
+ *   bytes, 256-byte aligned, which the caller zero-fills once before its
+ *   first use. Its first bytes hold per-chain counters through which the
+ *   sampling workgroups of one launch find the last of a chain's splits;
+ *   every call that completes leaves them zero and nothing else writes them,
+ *   so one buffer serves any number of calls of any sizes (within its size)
+ *   ordered on one stream. Calls that overlap in time on one buffer race.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
