@@ -19,11 +19,13 @@ ARCH = "gfx950"
 # Packed FP32 instructions stay off: the compiler must not form them.
 # Machine-level loop-invariant code motion stays off too: it hoists per-thread
 # addresses and constants out of the streaming loops into registers that stay
-# live across them (about 20 extra VGPRs in the streaming kernel).
+# live across them (about 20 extra VGPRs in the streaming kernel). Private
+# arrays are not moved to LDS: that costs occupancy instead of registers.
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-disable-machine-licm",
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wall", "-Wno-unused-function",
 ]
 

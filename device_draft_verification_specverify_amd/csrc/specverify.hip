@@ -491,6 +491,11 @@ __global__ __launch_bounds__(kBlock) void stream_kernel(StreamArgs a) {
           for (int q = 0; q < kVec; ++q) m = fmaxf(m, vec_elem<DT>(r[u], q));
 #pragma unroll
         for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+        // re-read the raw words below rather than keep 64 unpacked values live
+#pragma unroll
+        for (int u = 0; u < CL; ++u)
+#pragma unroll
+          for (int i = 0; i < (DT == SV_BF16 ? 4 : 8); ++i) asm volatile("" : "+v"(r[u].w[i]));
         double sum = 0.0;
         if (m != -INFINITY) {
           // 2^(z*k2 - c) with c = float(m*k2); d = m*k2 - c exactly (fma), and
@@ -590,23 +595,25 @@ __device__ __forceinline__ void top2_push(Top2& s, float key, int32_t id, float 
   s.d1 = b1 ? zd : s.d1;
 }
 
+// The best two of two sorted pairs, by selects only (no branches, so the
+// pair stays in registers).
 __device__ __forceinline__ Top2 top2_merge(const Top2& a, const Top2& b) {
+  const bool bf = cand_less(b.k1, b.i1, a.k1, a.i1);  // b holds the overall best
   Top2 r;
-  if (cand_less(b.k1, b.i1, a.k1, a.i1)) {
-    r.k1 = b.k1; r.i1 = b.i1; r.t1 = b.t1; r.d1 = b.d1;
-    const bool second_a = cand_less(a.k1, a.i1, b.k2, b.i2);
-    r.k2 = second_a ? a.k1 : b.k2;
-    r.i2 = second_a ? a.i1 : b.i2;
-    r.t2 = second_a ? a.t1 : b.t2;
-    r.d2 = second_a ? a.d1 : b.d2;
-  } else {
-    r.k1 = a.k1; r.i1 = a.i1; r.t1 = a.t1; r.d1 = a.d1;
-    const bool second_b = cand_less(b.k1, b.i1, a.k2, a.i2);
-    r.k2 = second_b ? b.k1 : a.k2;
-    r.i2 = second_b ? b.i1 : a.i2;
-    r.t2 = second_b ? b.t1 : a.t2;
-    r.d2 = second_b ? b.d1 : a.d2;
-  }
+  r.k1 = bf ? b.k1 : a.k1;
+  r.i1 = bf ? b.i1 : a.i1;
+  r.t1 = bf ? b.t1 : a.t1;
+  r.d1 = bf ? b.d1 : a.d1;
+  // second: the loser's best against the winner's second
+  const float xk = bf ? a.k1 : b.k1, yk = bf ? b.k2 : a.k2;
+  const int32_t xi = bf ? a.i1 : b.i1, yi = bf ? b.i2 : a.i2;
+  const float xt = bf ? a.t1 : b.t1, yt = bf ? b.t2 : a.t2;
+  const float xd = bf ? a.d1 : b.d1, yd = bf ? b.d2 : a.d2;
+  const bool xs = cand_less(xk, xi, yk, yi);
+  r.k2 = xs ? xk : yk;
+  r.i2 = xs ? xi : yi;
+  r.t2 = xs ? xt : yt;
+  r.d2 = xs ? xd : yd;
   return r;
 }
 
@@ -667,7 +674,7 @@ __device__ __forceinline__ void score_vec(const RawVec<DT>& rt, const RawVec<DT>
 
 // float64 score of candidate v with target / draft logits zt, zd:
 // ln w_v + G_v with G_v = -ln(-ln u_v).
-__device__ double rescore(bool residual, int32_t v, float zt, float zd, double T, double lzt,
+__device__ __forceinline__ double rescore(bool residual, int32_t v, float zt, float zd, double T, double lzt,
                           double lzd, uint32_t pos, uint32_t r, uint32_t s0, uint32_t s1) {
   if (v < 0 || v == INT_MAX) return -INFINITY;
   const Philox4 blk = philox4x32_10(uint32_t(v) >> 2, pos, r, kPurposeSample, s0, s1);
