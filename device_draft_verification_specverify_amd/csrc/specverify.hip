@@ -1,31 +1,31 @@
 // specverify.hip -- HIP kernels (gfx950 / CDNA4) and the C ABI of libspecverify.
 //
-// Batched speculative-sampling verification in three launches, none of which
-// hands data between workgroups inside a kernel (a kernel boundary is the only
-// cross-XCD synchronisation, so no L2 write-back fences are needed):
+// Batched speculative-sampling verification in three launches (a fourth only
+// past 65536 chains):
 //
-//   stream_kernel   every needed logit row is read exactly once. The flattened
-//                   space of (row, 8-logit vector) is cut into equal contiguous
-//                   ranges, one per resident wavefront, so every wavefront
-//                   streams the same number of bytes whatever the shape. Draft
-//                   rows of greedy batch rows are left out of that space. Each
-//                   lane keeps an online (max, sum of exp2) over its vectors
-//                   with one fma + one exp per logit; each row segment ends in
-//                   one cross-lane reduction and one 16-byte partial.
-//   chain_kernel    one workgroup per (chain, vocabulary split). It merges the
-//                   partials of its chain's rows into ln Z, gathers ln p / ln q
+//   stream_kernel   every needed logit row is read exactly once. Persistent
+//                   wavefronts walk 8 KB chunks of the flattened rows round
+//                   robin; draft rows of greedy batch rows are left out. Each
+//                   lane reduces its logits to (max, sum of exp2) with one fma +
+//                   one exp per logit; each chunk ends in one cross-lane
+//                   reduction and one 16-byte partial.
+//   accept_kernel   one workgroup per chain. It merges the partials of the
+//                   chain's rows into ln Z (each row once), gathers ln p / ln q
 //                   at the draft tokens, draws the accept uniforms and finds the
-//                   first rejection with one wavefront ballot (every split of a
-//                   chain computes the same n). Then it scans its split of the
-//                   one row pair the chain needs -- target/draft row n for the
-//                   residual, target row gamma for the bonus -- drawing Gumbel
-//                   noise by exponential race, argmin_v E_v / w_v with
-//                   E_v = -ln u_v (the same argmax as ln w_v + G_v), and keeps
-//                   its best two candidates.
-//                   The split re-scores those two in float64.
-//   finish_kernel   one wavefront per chain keeps the best float64 score over
-//                   the splits (ties to the lowest id).
+//                   first rejection n with one wavefront ballot.
+//   draw_kernel     one workgroup per (chain, vocabulary split). It scans its
+//                   split of the one row pair the chain needs -- target/draft
+//                   row n for the residual, target row gamma for the bonus --
+//                   drawing Gumbel noise by exponential race, argmin_v E_v / w_v
+//                   with E_v = -ln u_v (the same argmax as ln w_v + G_v), keeps
+//                   its best two candidates and re-scores them in float64. The
+//                   last split of a chain to finish (a per-chain counter) keeps
+//                   the best score over the splits (ties to the lowest id).
+//   finish_kernel   that last step, one wavefront per chain, when there are too
+//                   many chains for the counters.
 //
+// Hand-offs inside a launch (the per-chain counters) use relaxed agent-scope
+// atomics after the publishing wavefront's stores have completed.
 // No matrix cores (nothing here is a dense contraction) and no floating-point
 // atomics: results are bit-deterministic.
 
@@ -84,7 +84,7 @@ struct alignas(16) Cand {
   int32_t pad;
 };
 
-// What the finish kernel needs of a chain (written by split 0 of the chain kernel).
+// What the draw and finish kernels need of a chain (written by the accept kernel).
 struct alignas(16) ChainInfo {
   double lzt;  // ln Z of the target row the token is drawn from (row n, or gamma)
   double lzd;  // ln Z of draft row n (residual draws)
@@ -118,9 +118,11 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   return Philox4{{c0, c1, c2, c3}};
 }
 
-// u = (floor(w / 2^9) + 1/2) * 2^-23: exact in float and double.
+// u = (floor(w / 2^9) + 1/2) * 2^-23: exact in float and double. In float it is
+// built as (1 + m 2^-23) - (1 - 2^-24) with m = floor(w / 2^9) placed in the
+// mantissa of 1.0 by one funnel shift; the difference (2m + 1) 2^-24 is exact.
 __device__ __forceinline__ float unit_uniform(uint32_t w) {
-  return (float(w >> 9) + 0.5f) * 0x1p-23f;
+  return __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9u)) - 0x1.fffffep-1f;
 }
 __device__ __forceinline__ double unit_uniform_d(uint32_t w) {
   return (double(w >> 9) + 0.5) * 0x1p-23;
@@ -283,18 +285,16 @@ __device__ __forceinline__ void fold_partial(float& m, int32_t& idx, double& s, 
 
 // Statistics of NR stream rows (rho[r] < 0: none) by one wavefront: lane l
 // folds chunks l, l + 64, ... of each row, the loads of all NR rows issued
-// together; then the lanes combine in a fixed order. Every lane returns the
-// result. lnZ: ln sum exp(z / T) for T > 0, the raw maximum for T == 0, NaN
-// otherwise (an all -inf row gives -inf).
+// together; wave_reduce_row then combines the lanes of one row, and every lane
+// gets the result. lnZ: ln sum exp(z / T) for T > 0, the raw maximum for
+// T == 0, NaN otherwise (an all -inf row gives -inf).
 template <int NR>
-__device__ void wave_rows(const RowPartial* __restrict__ part, const int64_t (&rho)[NR],
-                          int64_t cpr, float T, RowStat (&out)[NR]) {
+__device__ __forceinline__ void lane_fold(const RowPartial* __restrict__ part,
+                                          const int64_t (&rho)[NR], int64_t cpr, float T,
+                                          float (&m)[NR], int32_t (&idx)[NR], double (&s)[NR]) {
   const int lane = threadIdx.x & (kWave - 1);
   const bool sampled = T > 0.0f;
   const double k2 = double(kLog2e / T);
-  float m[NR];
-  int32_t idx[NR];
-  double s[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     m[r] = -INFINITY;
@@ -309,28 +309,33 @@ __device__ void wave_rows(const RowPartial* __restrict__ part, const int64_t (&r
 #pragma unroll
     for (int r = 0; r < NR; ++r) fold_partial(m[r], idx[r], s[r], q[r], sampled, k2);
   }
+}
+
+// Combine the lanes' (m, idx, s) of one row in a fixed order.
+__device__ __forceinline__ RowStat wave_reduce_row(float m, int32_t idx, double s, float T) {
+  const bool sampled = T > 0.0f;
+  const double k2 = double(kLog2e / T);
+  float M = m;
+  int32_t I = idx;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    float M = m[r];
-    int32_t I = idx[r];
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const float om = __shfl_xor(M, off, kWave);
-      const int32_t oi = __shfl_xor(I, off, kWave);
-      better_max(M, I, om, oi);
-    }
-    double sr = 0.0;
-    if (sampled && M > -INFINITY) {
-      sr = m[r] > -INFINITY ? s[r] * exp2_scale((double(m[r]) - double(M)) * k2) : 0.0;
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
-    }
-    out[r].m = M;
-    out[r].idx = I;
-    if (sampled) out[r].lnz = M > -INFINITY ? double(M) / double(T) + log(sr) : double(M);
-    else if (T == 0.0f) out[r].lnz = double(M);
-    else out[r].lnz = NAN;
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const float om = __shfl_xor(M, off, kWave);
+    const int32_t oi = __shfl_xor(I, off, kWave);
+    better_max(M, I, om, oi);
   }
+  double sr = 0.0;
+  if (sampled && M > -INFINITY) {
+    sr = m > -INFINITY ? s * exp2_scale((double(m) - double(M)) * k2) : 0.0;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
+  }
+  RowStat out;
+  out.m = M;
+  out.idx = I;
+  if (sampled) out.lnz = M > -INFINITY ? double(M) / double(T) + log(sr) : double(M);
+  else if (T == 0.0f) out.lnz = double(M);
+  else out.lnz = NAN;
+  return out;
 }
 
 // ---------------------------------------------------------------------------
@@ -532,11 +537,15 @@ __global__ __launch_bounds__(kBlock) void finalize_rows_kernel(const RowPartial*
   const int64_t rho = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
   if (rho >= nrows) return;
   const int64_t rows[1] = {rho};
-  RowStat st[1];
-  wave_rows<1>(part, rows, cpr, temp[rho / P], st);
+  const float T = temp[rho / P];
+  float m[1];
+  int32_t idx[1];
+  double s[1];
+  lane_fold<1>(part, rows, cpr, T, m, idx, s);
+  const RowStat st = wave_reduce_row(m[0], idx[0], s[0], T);
   if ((threadIdx.x & (kWave - 1)) == 0) {
-    lnz[rho] = st[0].lnz;
-    if (amax) amax[rho] = st[0].idx == INT_MAX ? 0 : st[0].idx;
+    lnz[rho] = st.lnz;
+    if (amax) amax[rho] = st.idx == INT_MAX ? 0 : st.idx;
   }
 }
 
@@ -650,25 +659,25 @@ struct DrawParams {
 // E_v = -log2 u_v (a constant factor ln 2 does not move the argmin) and w_v
 // the unnormalised weight, 2^(z_t*k2 - L2t) = p_v for the bonus draw, and
 // p_v - q_v with q_v = p_v * 2^((z_d - z_t)*k2 + D2) for the residual draw.
-// PARTIAL: vi is a row's last, partial vector; ids >= V are skipped.
-template <int DT, bool RESIDUAL, bool PARTIAL>
+// Ids >= V (a row's last, partial vector) hold -inf logits (load_vec_bounded),
+// so their weight is 0 or NaN and their key +inf.
+template <int DT, bool RESIDUAL>
 __device__ __forceinline__ void score_vec(const RawVec<DT>& rt, const RawVec<DT>& rd, int64_t vi,
-                                          int64_t V, const DrawParams& dp, Top2& best) {
+                                          const DrawParams& dp, Top2& best) {
   const uint32_t c0 = uint32_t(vi * 2);
   const Philox4 lo = philox4x32_10(c0, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
   const Philox4 hi = philox4x32_10(c0 + 1u, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
 #pragma unroll
   for (int t = 0; t < kVec; ++t) {
     const float zt = vec_elem<DT>(rt, t);
+    const float zd = RESIDUAL ? vec_elem<DT>(rd, t) : 0.0f;
     const float a2 = fmaf(zt, dp.k2, -dp.L2t);
     float w = __builtin_amdgcn_exp2f(a2);
-    if constexpr (RESIDUAL)
-      w -= __builtin_amdgcn_exp2f(a2 + fmaf(vec_elem<DT>(rd, t) - zt, dp.k2, dp.D2));
+    if constexpr (RESIDUAL) w -= __builtin_amdgcn_exp2f(a2 + fmaf(zd - zt, dp.k2, dp.D2));
     const uint32_t word = t < 4 ? lo.w[t] : hi.w[t - 4];
     const float e2 = -__builtin_amdgcn_logf(unit_uniform(word));
-    float key = (w > 0.0f) ? e2 * __builtin_amdgcn_rcpf(w) : INFINITY;
-    if constexpr (PARTIAL) key = (vi * kVec + t < V) ? key : INFINITY;
-    top2_push(best, key, int32_t(vi * kVec + t), zt, RESIDUAL ? vec_elem<DT>(rd, t) : 0.0f);
+    const float key = w > 0.0f ? e2 * __builtin_amdgcn_rcpf(w) : INFINITY;
+    top2_push(best, key, int32_t(vi * kVec + t), zt, zd);
   }
 }
 
@@ -695,9 +704,11 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
                                              uint32_t s1) {
   const int lane = threadIdx.x & (kWave - 1);
   double sc = -INFINITY;
-  if (lane < 2)
-    sc = lane == 0 ? rescore(residual, all.i1, all.t1, all.d1, T, lzt, lzd, pos, r, s0, s1)
-                   : rescore(residual, all.i2, all.t2, all.d2, T, lzt, lzd, pos, r, s0, s1);
+  if (lane < 2) {
+    const bool first = lane == 0;
+    sc = rescore(residual, first ? all.i1 : all.i2, first ? all.t1 : all.t2,
+                 first ? all.d1 : all.d2, T, lzt, lzd, pos, r, s0, s1);
+  }
   const double sc2 = __shfl(sc, 1, kWave);
   Cand c{sc, all.i1, 0};
   if (sc2 > sc || (sc2 == sc && all.i2 < all.i1)) c = Cand{sc2, all.i2, 0};
@@ -705,15 +716,16 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
   return c;
 }
 
-// Scan one split of the row pair. Each wavefront takes a contiguous quarter of
-// the split and lane l reads vectors vi0 + kWave*it (it < kSampleIters), so
-// the loads of a lane share one address and differ by immediate offsets; all
-// of them are issued before any is scored.
+// Scan one split of the row pair (residual: target and draft row n; else the
+// target row alone). Each wavefront takes a contiguous quarter of the split and
+// lane l reads vectors vi0 + kWave*it (it < kSampleIters), so the loads of a
+// lane share one address and differ by immediate offsets; all of them are
+// issued before any is scored, and the scoring loop is not unrolled (it walks
+// a window of registers that shifts by one vector per pass).
 template <int DT, bool VEC, bool RESIDUAL>
 __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d, int64_t split,
                                            int64_t V, const DrawParams& dp) {
   const int64_t vpr = (V + kVec - 1) / kVec;
-  const bool partial_tail = (V % kVec) != 0;
   const int64_t vi0 = split * (kSplit / kVec) +
                       int64_t(threadIdx.x / kWave) * (kWave * kSampleIters) + (threadIdx.x & (kWave - 1));
   RawVec<DT> rt[kSampleIters], rd[kSampleIters];
@@ -722,20 +734,40 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
     const int64_t vi = vi0 + int64_t(kWave) * it;
     const bool inside = vi < vpr;
     rt[it] = inside ? load_vec_bounded<DT, VEC>(row_t, vi, V) : neg_inf_vec<DT>();
-    if constexpr (RESIDUAL) rd[it] = inside ? load_vec_bounded<DT, VEC>(row_d, vi, V) : rt[it];
+    rd[it] = inside && RESIDUAL ? load_vec_bounded<DT, VEC>(row_d, vi, V) : rt[it];
   }
   Top2 best = top2_empty();
-#pragma unroll
+#pragma unroll 1
   for (int it = 0; it < kSampleIters; ++it) {
     const int64_t vi = vi0 + int64_t(kWave) * it;
-    if (vi < vpr) {
-      if (partial_tail && vi == vpr - 1)
-        score_vec<DT, RESIDUAL, true>(rt[it], RESIDUAL ? rd[it] : rt[it], vi, V, dp, best);
-      else
-        score_vec<DT, RESIDUAL, false>(rt[it], RESIDUAL ? rd[it] : rt[it], vi, V, dp, best);
+    if (vi < vpr) score_vec<DT, RESIDUAL>(rt[0], rd[0], vi, dp, best);
+#pragma unroll
+    for (int q = 0; q + 1 < kSampleIters; ++q) {
+      rt[q] = rt[q + 1];
+      rd[q] = rd[q + 1];
     }
   }
   return best;
+}
+
+// The token drawn from p (target row at ln Z = lzt) by one wavefront over the
+// whole row: the fallback for an empty residual support, which only rounding
+// can produce (cold code: never fetched unless taken). Every lane returns the
+// id (INT_MAX if the row has no candidate).
+template <int DT, bool VEC>
+__device__ __forceinline__ int32_t draw_from_p(const void* row_t, int64_t V, double T, double lzt,
+                                            DrawParams dp) {
+  const int lane = threadIdx.x & (kWave - 1);
+  dp.D2 = 0.0f;
+  const int64_t vpr = (V + kVec - 1) / kVec;
+  Top2 fb = top2_empty();
+  for (int64_t vi = lane; vi < vpr; vi += kWave) {
+    const RawVec<DT> pt = load_vec_bounded<DT, VEC>(row_t, vi, V);
+    score_vec<DT, false>(pt, pt, vi, dp, fb);
+  }
+  fb = wave_top2(fb);
+  const int32_t id = rescore_top2(fb, false, T, lzt, 0.0, dp.pos, dp.r, dp.s0, dp.s1).id;
+  return __shfl(id, 0, kWave);
 }
 
 struct ChainArgs {
@@ -746,7 +778,7 @@ struct ChainArgs {
   const int32_t* tokens;     // [B, K, G]
   uint64_t seed;
   const int64_t* pos0;
-  // outputs (written by split 0)
+  // outputs (accept kernel; out_token of a sampled chain: draw kernel)
   int32_t* accept_len;
   int32_t* out_token;
   float* logp;
@@ -759,28 +791,33 @@ struct ChainArgs {
   const double* lnz_d_in;    // [B, K, G]
   const int32_t* amax_in;    // [B, G+1]
   const int32_t* n_in;       // [B, K]
-  // to the finish kernel
+  // accept kernel -> draw kernel (-> finish kernel)
   int64_t nsplit;
   Cand* cand;                // [B*K][nsplit]
-  ChainInfo* info;           // [B*K] (for finish_kernel)
+  ChainInfo* info;           // [B*K]
   uint32_t* cnt;             // [B*K] splits done per chain, or null: finish_kernel picks the token
 };
 
-// At least 4 waves per SIMD: a 256-thread workgroup per (chain, split) then
-// fits 16 workgroups' worth of waves per CU, so the usual grids run in one round.
-template <int DT, bool VEC, bool GIVEN>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void chain_kernel(ChainArgs a) {
+// One workgroup per chain: the normalisers of the chain's rows from the stream
+// partials, ln p / ln q at the draft tokens, the accept uniforms and the first
+// rejection by one wavefront ballot. It writes the chain's outputs and, for the
+// draw kernel, ChainInfo: n and the normalisers the draw needs. GIVEN
+// (specverify_residual_sample): n and the normalisers are inputs. Every row is
+// merged once per chain here, not once per vocabulary split.
+constexpr int kAcceptBlock = 1024;
+constexpr int kAcceptWaves = kAcceptBlock / kWave;
+constexpr int kAcceptRows = 2;  // rows per wavefront per pass
+static_assert(kAcceptWaves * kAcceptRows >= 17, "one pass covers a gamma = 8 chain");
+
+template <int DT, bool GIVEN>
+__global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   __shared__ double s_lnz[kMaxRowsPerChain];
   __shared__ int32_t s_amax[SV_MAX_GAMMA + 1];
   __shared__ int32_t s_bad;
   __shared__ int32_t s_n;
-  __shared__ Top2 s_top[kWavesPerBlock];
-  __shared__ uint32_t s_last;
   const RowSet& rs = a.rs;
-  const int64_t chain = blockIdx.x / a.nsplit;
-  const int64_t split = blockIdx.x - chain * a.nsplit;
+  const int64_t chain = blockIdx.x;
   const int64_t b = chain / rs.K;
   const int64_t k = chain - b * rs.K;
   const int G = int(rs.G);
@@ -790,7 +827,6 @@ void chain_kernel(ChainArgs a) {
   const float T = rs.temp[b];
   const bool sampled = T > 0.0f;
   const bool greedy = T == 0.0f;
-  const bool lead = split == 0;
 
   if (GIVEN) {
     if (t == 0) {
@@ -803,7 +839,7 @@ void chain_kernel(ChainArgs a) {
     }
     if (t < G) s_lnz[P + t] = a.lnz_d_in[chain * G + t];
     __syncthreads();
-    if (greedy && lead && t == 0 && s_n >= 0) a.out_token[chain] = s_amax[s_n];
+    if (greedy && t == 0 && s_n >= 0) a.out_token[chain] = s_amax[s_n];
   } else {
     // Loads that do not depend on the normalisers go first so their latency
     // overlaps the merges: draft tokens, the logits at them, accept uniforms.
@@ -827,33 +863,42 @@ void chain_kernel(ChainArgs a) {
     if (t >= P && t < P + G) s_lnz[t] = NAN;  // stays NaN for a greedy row's drafts
     __syncthreads();
     // normalisers of the chain's rows (target rows 0..G, then draft rows
-    // (k, 0..G-1) when sampled): wavefront w merges rows w, w + 4, ..., five
-    // at a time with all their partial loads issued together
+    // (k, 0..G-1) when sampled): wavefront w merges rows w, w + W, w + 2W
+    // (W wavefronts), with all their partial loads issued together
     {
       const int nr = P + (sampled ? G : 0);
       const int wv = t / kWave;
-      for (int base = wv; base < nr; base += 5 * kWavesPerBlock) {
-        int64_t rho[5];
+      for (int base = wv; base < nr; base += kAcceptRows * kAcceptWaves) {
+        int64_t rho[kAcceptRows];
 #pragma unroll
-        for (int r = 0; r < 5; ++r) {
-          const int ri = base + kWavesPerBlock * r;
+        for (int r = 0; r < kAcceptRows; ++r) {
+          const int ri = base + kAcceptWaves * r;
           rho[r] = ri >= nr ? -1 : ri < P ? b * P + ri : rs.B * P + chain * G + (ri - P);
         }
-        RowStat st[5];
-        wave_rows<5>(a.part, rho, a.cpr, T, st);
-        if (lane == 0) {
-#pragma unroll
-          for (int r = 0; r < 5; ++r) {
-            const int ri = base + kWavesPerBlock * r;
-            if (ri >= nr) continue;
-            s_lnz[ri] = st[r].lnz;
-            if (!(st[r].m > -INFINITY)) atomicOr(&s_bad, SV_ERR_ROW);
+        float m[kAcceptRows];
+        int32_t idx[kAcceptRows];
+        double s[kAcceptRows];
+        lane_fold<kAcceptRows>(a.part, rho, a.cpr, T, m, idx, s);
+        // rows one at a time through a shifting window (rolled: less code)
+#pragma unroll 1
+        for (int r = 0; r < kAcceptRows; ++r) {
+          const RowStat st = wave_reduce_row(m[0], idx[0], s[0], T);
+          const int ri = base + kAcceptWaves * r;
+          if (lane == 0 && ri < nr) {
+            s_lnz[ri] = st.lnz;
+            if (!(st.m > -INFINITY)) atomicOr(&s_bad, SV_ERR_ROW);
             if (ri < P) {
-              s_amax[ri] = st[r].idx == INT_MAX ? 0 : st[r].idx;
-              if (lead && k == 0 && a.lnz_t_out) a.lnz_t_out[b * P + ri] = st[r].lnz;
-            } else if (lead && a.lnz_d_out) {
-              a.lnz_d_out[chain * G + (ri - P)] = st[r].lnz;
+              s_amax[ri] = st.idx == INT_MAX ? 0 : st.idx;
+              if (k == 0 && a.lnz_t_out) a.lnz_t_out[b * P + ri] = st.lnz;
+            } else if (a.lnz_d_out) {
+              a.lnz_d_out[chain * G + (ri - P)] = st.lnz;
             }
+          }
+#pragma unroll
+          for (int q = 0; q + 1 < kAcceptRows; ++q) {
+            m[q] = m[q + 1];
+            idx[q] = idx[q + 1];
+            s[q] = s[q + 1];
           }
         }
       }
@@ -876,8 +921,8 @@ void chain_kernel(ChainArgs a) {
             lq = 0.0;
           }
         }
-        if (lead && a.logp) a.logp[chain * G + j] = float(lp);
-        if (lead && a.logq) a.logq[chain * G + j] = float(lq);
+        if (a.logp) a.logp[chain * G + j] = float(lp);
+        if (a.logq) a.logq[chain * G + j] = float(lq);
       }
       const uint64_t acc_mask = __ballot(acc);
       const uint64_t bad_mask = __ballot(tok_bad);
@@ -887,23 +932,21 @@ void chain_kernel(ChainArgs a) {
         if (bad_mask) err |= SV_ERR_TOKEN;
         if (!(sampled || greedy)) err |= SV_ERR_TEMP;
         s_n = err ? -1 : n;
-        if (lead) {
-          if (err) {
-            a.accept_len[chain] = -1;
-            a.out_token[chain] = -1;
-            if (a.dev_err) atomicOr(a.dev_err, err);
-          } else {
-            a.accept_len[chain] = n;
-            if (greedy) a.out_token[chain] = s_amax[n];
-          }
+        if (err) {
+          a.accept_len[chain] = -1;
+          a.out_token[chain] = -1;
+          if (a.dev_err) atomicOr(a.dev_err, err);
+        } else {
+          a.accept_len[chain] = n;
+          if (greedy) a.out_token[chain] = s_amax[n];
         }
       }
     }
     __syncthreads();
   }
 
-  const int n = s_n;
-  if (lead && t == 0) {
+  if (t == 0) {
+    const int n = s_n;
     ChainInfo ci;
     ci.n = (n >= 0 && sampled) ? n : -1;
     ci.lzt = n >= 0 ? s_lnz[n] : 0.0;
@@ -911,15 +954,37 @@ void chain_kernel(ChainArgs a) {
     ci.pad[0] = ci.pad[1] = ci.pad[2] = 0;
     a.info[chain] = ci;
   }
-  if (n < 0 || !sampled) return;  // uniform across the workgroup
+}
+
+// One workgroup per (chain, split of kSplit ids) of every chain that draws.
+// At least 4 waves per SIMD: 16 workgroups' worth of waves per CU, so the
+// usual grids run in one round.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void draw_kernel(ChainArgs a) {
+  constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  __shared__ Top2 s_top[kWavesPerBlock];
+  __shared__ uint32_t s_last;
+  const RowSet& rs = a.rs;
+  const int64_t chain = blockIdx.x / a.nsplit;
+  const int64_t split = blockIdx.x - chain * a.nsplit;
+  const ChainInfo ci = a.info[chain];
+  const int n = ci.n;
+  if (n < 0) return;  // uniform across the workgroup: this chain draws nothing
+  const int64_t b = chain / rs.K;
+  const int64_t k = chain - b * rs.K;
+  const int G = int(rs.G);
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const float T = rs.temp[b];
 
   // Scan this split of the row pair, then re-score its best two in float64.
   const bool residual = n < G;
   const void* row_t = row_ptr(rs.t, esz, b * rs.tsb + int64_t(n) * rs.tsj);
   const void* row_d =
       residual ? row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + int64_t(n) * rs.dsj) : row_t;
-  const double lzt = s_lnz[n];
-  const double lzd = residual ? s_lnz[P + n] : 0.0;
+  const double lzt = ci.lzt;
+  const double lzd = residual ? ci.lzd : 0.0;
   DrawParams dp;
   dp.k2 = kLog2e / T;
   dp.L2t = float(lzt * kLog2eD);
@@ -973,19 +1038,7 @@ void chain_kernel(ChainArgs a) {
       id = oi;
     }
   }
-  if (id == INT_MAX) {
-    DrawParams fp = dp;
-    fp.D2 = 0.0f;
-    const int64_t vpr = (a.V + kVec - 1) / kVec;
-    Top2 fb = top2_empty();
-    for (int64_t vi = lane; vi < vpr; vi += kWave) {
-      const RawVec<DT> pt = load_vec_bounded<DT, VEC>(row_t, vi, a.V);
-      score_vec<DT, false, true>(pt, pt, vi, a.V, fp, fb);
-    }
-    fb = wave_top2(fb);
-    id = rescore_top2(fb, false, double(T), lzt, 0.0, fp.pos, fp.r, fp.s0, fp.s1).id;
-    id = __shfl(id, 0, kWave);
-  }
+  if (id == INT_MAX) id = draw_from_p<DT, VEC>(row_t, a.V, double(T), lzt, dp);
   if (lane == 0) a.out_token[chain] = id == INT_MAX ? -1 : id;
 }
 
@@ -1038,15 +1091,7 @@ __global__ __launch_bounds__(kWave) void finish_kernel(const void* tgt, int64_t 
     dp.r = uint32_t(chain);
     dp.s0 = uint32_t(seed);
     dp.s1 = uint32_t(seed >> 32);
-    const int64_t vpr = (V + kVec - 1) / kVec;
-    Top2 fb = top2_empty();
-    for (int64_t vi = lane; vi < vpr; vi += kWave) {
-      const RawVec<DT> pt = load_vec_bounded<DT, VEC>(row_t, vi, V);
-      score_vec<DT, false, true>(pt, pt, vi, V, dp, fb);
-    }
-    fb = wave_top2(fb);
-    id = rescore_top2(fb, false, double(T), ci.lzt, 0.0, dp.pos, dp.r, dp.s0, dp.s1).id;
-    id = __shfl(id, 0, kWave);
+    id = draw_from_p<DT, VEC>(row_t, V, double(T), ci.lzt, dp);
   }
   if (lane == 0) out_token[chain] = id == INT_MAX ? -1 : id;
 }
@@ -1166,9 +1211,11 @@ void launch_stream(int dtype, bool vec, bool argmax_all, const StreamArgs& sa, h
 template <int DT, bool VEC>
 void launch_chain_finish(const ChainArgs& ca, bool given, hipStream_t st) {
   const int64_t chains = ca.rs.B * ca.rs.K;
+  const dim3 one{unsigned(chains), 1u, 1u};
+  if (given) hipLaunchKernelGGL((accept_kernel<DT, true>), one, dim3(kAcceptBlock), 0, st, ca);
+  else hipLaunchKernelGGL((accept_kernel<DT, false>), one, dim3(kAcceptBlock), 0, st, ca);
   const dim3 grid{unsigned(chains * ca.nsplit), 1u, 1u};
-  if (given) hipLaunchKernelGGL((chain_kernel<DT, VEC, true>), grid, dim3(kBlock), 0, st, ca);
-  else hipLaunchKernelGGL((chain_kernel<DT, VEC, false>), grid, dim3(kBlock), 0, st, ca);
+  hipLaunchKernelGGL((draw_kernel<DT, VEC>), grid, dim3(kBlock), 0, st, ca);
   if (ca.cnt) return;  // the chains' last splits picked the tokens
   const RowSet& rs = ca.rs;
   hipLaunchKernelGGL((finish_kernel<DT, VEC>), dim3(unsigned(chains)), dim3(kWave), 0, st, rs.t,
