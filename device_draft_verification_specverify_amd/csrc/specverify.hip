@@ -44,6 +44,13 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
+// The streaming kernel runs one 1024-thread workgroup per CU whose wavefronts
+// claim chunks from an LDS counter. A SIMD issues the memory instructions of
+// its older wavefronts first, so with a fixed share per wavefront the youngest
+// read at less than half the rate of the oldest and finish ~20 us later
+// (measured: six 256-thread workgroups per CU, round-robin chunks).
+constexpr int kStreamBlock = 1024;
+constexpr int kStreamWaves = kStreamBlock / kWave;
 constexpr int kVec = 8;                    // logits per vector (16 B of bf16, 32 B of f32)
 constexpr int kSampleIters = 4;            // vectors per thread per sampling split
 constexpr int64_t kSplit = int64_t(kBlock) * kVec * kSampleIters;  // 8192 ids per split
@@ -344,14 +351,14 @@ __device__ __forceinline__ RowStat wave_reduce_row(float m, int32_t idx, double 
 struct SampledTable {
   uint64_t mask[kMaxCompactB / 64];
   int32_t pref[kMaxCompactB / 64 + 1];
-  int32_t wsum[kWavesPerBlock];
+  int32_t wsum[kStreamWaves];
 };
 
 __device__ void build_sampled_table(const float* __restrict__ temp, int64_t B, SampledTable& tab) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const int nchunks = int((B + 63) / 64);
-  for (int c = wid; c < nchunks; c += kWavesPerBlock) {
+  for (int c = wid; c < nchunks; c += kStreamWaves) {
     const int64_t b = int64_t(c) * 64 + lane;
     const bool s = b < B && temp[b] > 0.0f;
     const uint64_t m = __ballot(s);
@@ -396,14 +403,15 @@ struct StreamArgs {
   int32_t* rank_out;     // [B + 1]: sampled batch rows before b; [B] = their total
 };
 
-// Persistent wavefronts walk the chunks of the flattened stream round robin
-// (wavefront w takes chunks w, w + W, w + 2W, ...), so at any moment the grid
-// reads one moving window of the rows. A chunk's loads are all issued before
-// any is used. Sampled rows: chunk maximum M and s = sum 2^((z - M) * k2);
+// Persistent workgroups (one per CU) walk the chunks of the flattened stream
+// round robin (workgroup g owns chunks g, g + G, g + 2G, ...; its wavefronts
+// claim them in order), so at any moment the grid reads one moving window of
+// the rows. A chunk's loads are all issued before any is used. Sampled rows: chunk maximum M and s = sum 2^((z - M) * k2);
 // greedy rows: maximum and lowest argmax; ARGMAX_ALL: argmax of sampled rows too.
 template <int DT, bool VEC, bool ARGMAX_ALL>
-__global__ __launch_bounds__(kBlock) void stream_kernel(StreamArgs a) {
+__global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
   __shared__ SampledTable tab;
+  __shared__ uint32_t s_claim;
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   constexpr int CL = chunk_lanes<DT>();
   const RowSet& rs = a.rs;
@@ -412,11 +420,13 @@ __global__ __launch_bounds__(kBlock) void stream_kernel(StreamArgs a) {
   const int64_t KG = rs.K * rs.G;
   const int nchunks = int((rs.B + 63) / 64);
   int64_t nrows = a.nrows;
+  if (threadIdx.x == 0) s_claim = 0u;
+  __syncthreads();
   if (a.compact) {
     build_sampled_table(rs.temp, rs.B, tab);
     nrows = BP + int64_t(tab.pref[nchunks]) * KG;
     if (blockIdx.x == 0 && a.rank_out) {
-      for (int64_t b = threadIdx.x; b < rs.B; b += kBlock) {
+      for (int64_t b = threadIdx.x; b < rs.B; b += kStreamBlock) {
         const int c = int(b >> 6);
         a.rank_out[b] = tab.pref[c] + __popcll(tab.mask[c] & ((1ull << (b & 63)) - 1ull));
       }
@@ -425,9 +435,15 @@ __global__ __launch_bounds__(kBlock) void stream_kernel(StreamArgs a) {
   }
   const int64_t cv = int64_t(kWave) * CL;
   const int64_t total = nrows * a.cpr;
-  const int64_t W = int64_t(gridDim.x) * kWavesPerBlock;
+  const int64_t nblk = gridDim.x;
   const bool v_tail = (a.V % kVec) != 0;
-  for (int64_t c = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6); c < total; c += W) {
+  // workgroup g owns chunks g, g + nblk, ...; its wavefronts claim them in order
+  uint32_t claim = 0;
+  if (lane == 0) claim = atomicAdd(&s_claim, 1u);
+  int64_t c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(claim));
+  while (c < total) {
+    uint32_t next = 0;
+    if (lane == 0) next = atomicAdd(&s_claim, 1u);  // the next claim, answered during the loads
     const int64_t rho = c / a.cpr;
     const int64_t v0 = (c - rho * a.cpr) * cv;
     const int64_t v1 = v0 + cv < a.vpr ? v0 + cv : a.vpr;
@@ -525,6 +541,7 @@ __global__ __launch_bounds__(kBlock) void stream_kernel(StreamArgs a) {
       }
     }
     if (lane == 0) a.part[slot * a.cpr + (c - rho * a.cpr)] = out;
+    c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(next));
   }
 }
 
@@ -1171,9 +1188,9 @@ int64_t stream_blocks() {
     cus = 256;
   int blocks = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<DT, VEC, ARGMAX_ALL>,
-                                                   kBlock, 0) != hipSuccess ||
+                                                   kStreamBlock, 0) != hipSuccess ||
       blocks <= 0)
-    blocks = 4;
+    blocks = 1;
   const int64_t n = int64_t(cus) * blocks;
   if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
@@ -1188,10 +1205,10 @@ int launch_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP; 
 template <int DT, bool VEC, bool ARGMAX_ALL>
 void launch_stream_t(const StreamArgs& sa, hipStream_t st) {
   int64_t grid = stream_blocks<DT, VEC, ARGMAX_ALL>();
-  const int64_t need = (sa.nrows * sa.cpr + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t need = (sa.nrows * sa.cpr + kStreamWaves - 1) / kStreamWaves;
   if (grid > need) grid = need;
-  hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(grid)), dim3(kBlock), 0,
-                     st, sa);
+  hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(grid)),
+                     dim3(kStreamBlock), 0, st, sa);
 }
 
 void launch_stream(int dtype, bool vec, bool argmax_all, const StreamArgs& sa, hipStream_t st) {
