@@ -7,13 +7,18 @@ before timing.
 
 Prints one JSON line: verified draft tokens/s (B*gamma per step) and the HBM
 roofline of the dominant kernel, plus the fp64 CPU oracle timed on a bounded
-sample as a reported baseline.
+sample as a reported baseline. `per_config` adds every workload (C1-C5, and the
+accept test alone on C4's log-probabilities) timed cold: before each of the
+timed reps a 512 MiB buffer is rewritten, which evicts the 256 MB last-level
+cache and the L2s, and HIP events bracket the step alone (median, p10, p90).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--copies C] [--no-cpu]
+                    [--per-config all|none|c1,c3,...] [--reps R]
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import hashlib
 import json
 import os
@@ -73,20 +78,104 @@ def stacked_inputs(w, dev):
     return buf, buf[:, : g + 1], buf[:, g + 1:].unsqueeze(1)
 
 
-def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 3) -> dict:
+def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 300) -> dict:
+    """The oracle as it is, on the host's cores: one thread per slice of batch rows
+    (NumPy releases the GIL inside its array operations), whole steps repeated
+    until min_seconds have passed."""
     import oracle
 
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    slices = [r for r in np.array_split(np.arange(w.B), threads) if len(r)]
+
+    def run(rows):
+        return oracle.verify(w.target[rows], w.draft[rows], w.tokens[rows], w.temperature[rows],
+                             w.seed, w.pos0[rows], batch_index=rows, dtype=w.dtype)
+
     reps, t0 = 0, time.perf_counter()
-    while reps < max_reps:
-        oracle.verify(w.target, w.draft, w.tokens, w.temperature, w.seed, w.pos0, dtype=w.dtype)
-        reps += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(slices)) as ex:
+        while reps < max_reps:
+            list(ex.map(run, slices))
+            reps += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
     dt = (time.perf_counter() - t0) / reps
-    return {"value": w.B * w.K * w.gamma / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": w.B * w.K * w.gamma / dt, "unit": "tokens/s", "cores": len(slices),
+            "kind": "oracle",
             "sample": f"{reps} full step(s) of the benchmark workload ({w.B} chains, "
-                      f"{w.B * w.K * w.gamma} draft tokens), NumPy float64, single thread",
-            "seconds_per_step": dt}
+                      f"{w.B * w.K * w.gamma} draft tokens), NumPy float64, one thread per "
+                      f"slice of batch rows",
+            "seconds_per_step": dt, "gbps": algorithmic_bytes(w) / dt / 1e9}
+
+
+def device_logits(raw: np.ndarray, dtype: str, dev) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(raw.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(raw).to(dev)
+
+
+def pct(xs, q) -> float:
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def cold_times_us(fn, reps: int, warmup: int, scratch: torch.Tensor, stream) -> list:
+    """HIP-event time of fn() per rep, each after a 512 MiB rewrite of scratch."""
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps):
+        scratch.fill_(i & 0xFF)
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [1e3 * a.elapsed_time(b) for a, b in ev]
+
+
+def per_config(names, reps: int, warmup: int, dev) -> dict:
+    """Every workload's step timed cold; C4 also times the accept test alone."""
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    res = {}
+    for name in names:
+        w = workloads.make(name)
+        tgt = device_logits(w.target, w.dtype, dev)
+        dft = device_logits(w.draft, w.dtype, dev)
+        tokens = torch.from_numpy(w.tokens).to(dev)
+        temp = torch.from_numpy(w.temperature).to(dev)
+        pos0 = torch.from_numpy(w.pos0).to(dev)
+        plan = sv.StepPlan(tgt, dft, tokens, temp, w.seed, pos0)
+        us = cold_times_us(plan, reps, warmup, scratch, stream)
+        med = pct(us, 50)
+        # back-to-back steps on the same inputs (warm caches), for the launch-bound sizes
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            plan()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        warm = 1e3 * e0.elapsed_time(e1) / 20
+        nbytes = algorithmic_bytes(w)
+        entry = {"B": w.B, "K": w.K, "gamma": w.gamma, "V": w.V, "logits": w.dtype,
+                 "us_median": med, "us_p10": pct(us, 10), "us_p90": pct(us, 90),
+                 "us_warm_back_to_back": warm,
+                 "tokens_per_s": w.B * w.K * w.gamma / (med * 1e-6),
+                 "bytes_min": nbytes, "hbm_gbps": nbytes / (med * 1e-6) / 1e9,
+                 "hbm_frac_of_peak": nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                 "device_error": int(plan.out.device_error.item())}
+        res[name] = entry
+        if name == "c4":
+            # the accept test alone on this step's [B, K, gamma] log-probabilities
+            lp, lq = plan.out.logp.clone(), plan.out.logq.clone()
+            acc = cold_times_us(lambda: sv.specverify_accept(lp, lq, w.seed, pos0), reps, warmup,
+                                scratch, stream)
+            res["c4_accept_only"] = {"B": w.B, "K": w.K, "gamma": w.gamma,
+                                     "us_median": pct(acc, 50), "us_p10": pct(acc, 10),
+                                     "us_p90": pct(acc, 90),
+                                     "decisions_per_call": w.B * w.K * w.gamma}
+        del plan, tgt, dft
+        torch.cuda.empty_cache()
+    return res
 
 
 def main() -> int:
@@ -97,6 +186,9 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=4,
                     help="input copies cycled so consecutive steps never reuse cached logits")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--per-config", default="all",
+                    help="'all', 'none', or a comma list of c1..c5 timed cold after the main run")
+    ap.add_argument("--reps", type=int, default=50, help="timed reps per workload in per_config")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"after timing, copy {COPY_BYTES} bytes three times (counter scaling)")
     args = ap.parse_args()
@@ -187,6 +279,10 @@ def main() -> int:
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
                      "bytes_per_launch": kernel_bytes, "avg_launch_ms": kern_ms},
     }
+    if args.per_config != "none":
+        names = (list(workloads.CONFIGS) if args.per_config == "all"
+                 else [n for n in args.per_config.split(",") if n])
+        line["per_config"] = per_config(names, args.reps, 10, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
