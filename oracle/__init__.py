@@ -14,3 +14,4 @@ from . import philox  # noqa: F401
 from .specverify import (  # noqa: F401
     ACCEPT, SAMPLE, FLAG_EPS, decode_logits, normalize_rows, accept_from_logprobs, verify,
 )
+from .acceptance import acceptance_probability, outcome_law, expected_accept_length  # noqa: F401
