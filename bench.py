@@ -163,6 +163,17 @@ def per_config(names, reps: int, warmup: int, dev) -> dict:
                  "bytes_min": nbytes, "hbm_gbps": nbytes / (med * 1e-6) / 1e9,
                  "hbm_frac_of_peak": nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                  "device_error": int(plan.out.device_error.item())}
+        # the acceptance probability and accept-length law of the same step's rows
+        lz_t = plan.out.lnZ_target.clone()
+        lz_d = torch.nan_to_num(plan.out.lnZ_draft, nan=0.0)
+        aws = sv.accept_prob_workspace(w.B, w.K, w.gamma, w.V, plan.dtype, dev)
+        ap = cold_times_us(lambda: sv.specverify_accept_prob(tgt, dft, temp, lz_t, lz_d, ws=aws),
+                           reps, warmup, scratch, stream)
+        ap_bytes = (w.B * w.gamma * w.V + w.B * w.K * w.gamma * w.V) * w.bytes_per_logit
+        entry["accept_prob"] = {"us_median": pct(ap, 50), "us_p10": pct(ap, 10),
+                                "us_p90": pct(ap, 90), "bytes_min": ap_bytes,
+                                "hbm_gbps": ap_bytes / (pct(ap, 50) * 1e-6) / 1e9}
+        del aws
         res[name] = entry
         if name == "c4":
             # the accept test alone on this step's [B, K, gamma] log-probabilities

@@ -42,6 +42,9 @@ _SIGNATURES = {
                                           _P]),
     "specverify_step": (_INT, [_P, _P, _INT, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                _I64, _P, _U64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "specverify_accept_prob_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
+    "specverify_accept_prob": (_INT, [_P, _P, _INT, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                      _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "specverify_status_string": (ctypes.c_char_p, [_INT]),
     "specverify_version": (_INT, []),
 }
@@ -250,6 +253,43 @@ class StepPlan:
 def specverify_step(target, draft, tokens, temperature, seed: int, pos0=None, **kw) -> StepOutputs:
     """One fused verification step (allocates its outputs and workspace)."""
     return StepPlan(target, draft, tokens, temperature, seed, pos0, **kw)()
+
+
+def accept_prob_workspace(B: int, K: int, gamma: int, V: int, dtype: int, device) -> torch.Tensor:
+    n = int(load_library().specverify_accept_prob_workspace_size(B, K, gamma, V, dtype))
+    if n == 0:
+        raise SpecVerifyError("sizes rejected by specverify_accept_prob_workspace_size")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def specverify_accept_prob(target: torch.Tensor, draft: torch.Tensor, temperature: torch.Tensor,
+                           lnZ_target: torch.Tensor, lnZ_draft: torch.Tensor,
+                           want_law: bool = True, ws: torch.Tensor | None = None):
+    """alpha [B, K, gamma] float64 (and the accept-length law [B, K, gamma+1]) from the
+    logits of a step and its normalisers (lnZ_target [B, gamma+1], lnZ_draft [B, K, gamma])."""
+    lib = load_library()
+    _logits(target, 3, "target")
+    _logits(draft, 4, "draft")
+    B, G1, V = target.shape
+    K, g = draft.shape[1], draft.shape[2]
+    if G1 != g + 1 or draft.shape[0] != B or draft.shape[3] != V or draft.dtype != target.dtype:
+        raise SpecVerifyError("target [B, gamma+1, V] and draft [B, K, gamma, V] disagree")
+    _need(temperature, torch.float32, (B,), "temperature")
+    _need(lnZ_target, torch.float64, (B, g + 1), "lnZ_target")
+    _need(lnZ_draft, torch.float64, (B, K, g), "lnZ_draft")
+    dt = _dtype_code(target)
+    dev = target.device
+    if ws is None:
+        ws = accept_prob_workspace(B, K, g, V, dt, dev)
+    alpha = torch.empty((B, K, g), dtype=torch.float64, device=dev)
+    law = torch.empty((B, K, g + 1), dtype=torch.float64, device=dev) if want_law else None
+    st = lib.specverify_accept_prob(
+        target.data_ptr(), draft.data_ptr(), dt, B, K, g, V, target.stride(0), target.stride(1),
+        draft.stride(0), draft.stride(1), draft.stride(2), temperature.data_ptr(),
+        lnZ_target.data_ptr(), lnZ_draft.data_ptr(), alpha.data_ptr(), _ptr(law), ws.data_ptr(),
+        ws.numel(), _stream(dev))
+    _check(st, "specverify_accept_prob")
+    return alpha, law
 
 
 def version() -> int:

@@ -1139,6 +1139,221 @@ __global__ __launch_bounds__(kBlock) void accept_scalar_kernel(const float* __re
 }
 
 // ---------------------------------------------------------------------------
+// Acceptance probability alpha_j = sum_v min(p_j(v), q_j(v)) per chain and draft
+// position, and the accept-length law P(n = m) = alpha_0..alpha_{m-1} (1 - alpha_m)
+// (P(n = gamma) = alpha_0..alpha_{gamma-1}), from the normalisers of a step.
+
+// Per (chain, position, chunk): the chunk's sum of min(p, q) (sampled rows), or
+// the chunk maxima and their lowest ids of the target and draft rows (greedy).
+struct alignas(8) OverlapPartial {
+  double s;
+  float mt, md;
+  int32_t it, id;
+};
+
+struct OverlapArgs {
+  RowSet rs;
+  int64_t V, vpr, cpr;
+  const double* lnz_t;     // [B, G+1]
+  const double* lnz_d;     // [B, K, G]
+  OverlapPartial* part;    // [(b*K + k)*G + j][cpr]
+};
+
+// One sweep over the target rows 0..G-1 and every draft row. A unit is
+// (b, j, chunk): the target chunk is loaded once and kept in registers while
+// the K draft chunks of the same (b, j) are read against it. Since 2^x is
+// increasing, min(p, q) = 2^min(e_p, e_q) with e = (z / T - ln Z) log2(e): one
+// exp2 per pair. Each lane writes e = (z - m) k + (m k - ln Z log2 e) around its
+// own largest logit m, with the offset in float64, so the float32 exponent
+// carries no cancellation error where the terms are large; per-vector sums
+// in float32, lane sums in float64. Persistent: one workgroup per CU claiming
+// units from an LDS counter.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
+  __shared__ uint32_t s_claim;
+  constexpr int CL = chunk_lanes<DT>();
+  const RowSet& rs = a.rs;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (threadIdx.x == 0) s_claim = 0u;
+  __syncthreads();
+  const int64_t G = rs.G;
+  const int64_t cv = int64_t(kWave) * CL;
+  const int64_t total = rs.B * G * a.cpr;
+  const int64_t nblk = gridDim.x;
+  const bool v_tail = (a.V % kVec) != 0;
+  constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  uint32_t claim = 0;
+  if (lane == 0) claim = atomicAdd(&s_claim, 1u);
+  int64_t c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(claim));
+  while (c < total) {
+    uint32_t next = 0;
+    if (lane == 0) next = atomicAdd(&s_claim, 1u);
+    const int64_t bj = c / a.cpr;
+    const int64_t chunk = c - bj * a.cpr;
+    const int64_t b = bj / G;
+    const int64_t j = bj - b * G;
+    const int64_t v0 = chunk * cv;
+    const int64_t v1 = v0 + cv < a.vpr ? v0 + cv : a.vpr;
+    const float T = rs.temp[b];
+    const bool sampled = T > 0.0f;
+    const void* trow = row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj);
+    RawVec<DT> rt[CL];
+#pragma unroll
+    for (int u = 0; u < CL; ++u) {
+      const int64_t vi = v0 + lane + int64_t(kWave) * u;
+      if (vi >= v1) rt[u] = neg_inf_vec<DT>();
+      else if (v_tail && vi == a.vpr - 1) rt[u] = load_vec_bounded<DT, VEC>(trow, vi, a.V);
+      else rt[u] = load_vec<DT, VEC, true>(trow, vi);
+    }
+    const double k2 = kLog2eD / double(T);
+    const float k2f = float(k2);
+    const double l2t = sampled ? a.lnz_t[b * (G + 1) + j] * kLog2eD : 0.0;
+    // greedy rows: the target chunk's maximum and lowest id, shared by the K drafts
+    float tm = -INFINITY;
+    int32_t ti = INT_MAX;
+    if (!sampled) {
+#pragma unroll
+      for (int u = 0; u < CL; ++u)
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) {
+          const float x = vec_elem<DT>(rt[u], q);
+          if (x > tm) {
+            tm = x;
+            ti = int32_t((v0 + lane + int64_t(kWave) * u) * kVec + q);
+          }
+        }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        const float om = __shfl_xor(tm, off, kWave);
+        const int32_t oi = __shfl_xor(ti, off, kWave);
+        better_max(tm, ti, om, oi);
+      }
+    }
+    for (int64_t k = 0; k < rs.K; ++k) {
+      const int64_t chain = b * rs.K + k;
+      const void* drow = row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj);
+      RawVec<DT> rd[CL];
+#pragma unroll
+      for (int u = 0; u < CL; ++u) {
+        const int64_t vi = v0 + lane + int64_t(kWave) * u;
+        if (vi >= v1) rd[u] = neg_inf_vec<DT>();
+        else if (v_tail && vi == a.vpr - 1) rd[u] = load_vec_bounded<DT, VEC>(drow, vi, a.V);
+        else rd[u] = load_vec<DT, VEC, true>(drow, vi);
+      }
+      OverlapPartial out{0.0, tm, -INFINITY, ti, INT_MAX};
+      if (sampled) {
+        const double l2d = a.lnz_d[chain * G + j] * kLog2eD;
+        float m = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < CL; ++u)
+#pragma unroll
+          for (int q = 0; q < kVec; ++q)
+            m = fmaxf(m, fmaxf(vec_elem<DT>(rt[u], q), vec_elem<DT>(rd[u], q)));
+        // re-read the raw words below rather than keep 128 unpacked values live
+#pragma unroll
+        for (int u = 0; u < CL; ++u)
+#pragma unroll
+          for (int i = 0; i < (DT == SV_BF16 ? 4 : 8); ++i) {
+            asm volatile("" : "+v"(rt[u].w[i]));
+            asm volatile("" : "+v"(rd[u].w[i]));
+          }
+        double sum = 0.0;
+        if (m > -INFINITY) {
+          const double mk = double(m) * k2;
+          const float at = float(mk - l2t);
+          const float ad = float(mk - l2d);
+#pragma unroll
+          for (int u = 0; u < CL; ++u) {
+            float sv = 0.0f;
+#pragma unroll
+            for (int q = 0; q < kVec; ++q) {
+              // -inf logits (and ids past V) give exp2(-inf) = 0
+              const float ep = fmaf(vec_elem<DT>(rt[u], q) - m, k2f, at);
+              const float eq = fmaf(vec_elem<DT>(rd[u], q) - m, k2f, ad);
+              sv += __builtin_amdgcn_exp2f(fminf(ep, eq));
+            }
+            sum += double(sv);
+          }
+        }
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+        out.s = sum;
+      } else {
+        float dm = -INFINITY;
+        int32_t di = INT_MAX;
+#pragma unroll
+        for (int u = 0; u < CL; ++u)
+#pragma unroll
+          for (int q = 0; q < kVec; ++q) {
+            const float x = vec_elem<DT>(rd[u], q);
+            if (x > dm) {
+              dm = x;
+              di = int32_t((v0 + lane + int64_t(kWave) * u) * kVec + q);
+            }
+          }
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) {
+          const float om = __shfl_xor(dm, off, kWave);
+          const int32_t oi = __shfl_xor(di, off, kWave);
+          better_max(dm, di, om, oi);
+        }
+        out.md = dm;
+        out.id = di;
+      }
+      if (lane == 0) a.part[(chain * G + j) * a.cpr + chunk] = out;
+    }
+    c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(next));
+  }
+}
+
+// One wavefront per chain: alpha_j from the chunk partials (a fixed-order
+// float64 sum; greedy rows: do the two rows' lowest argmaxes agree), then the
+// accept-length law.
+__global__ __launch_bounds__(kBlock) void alpha_law_kernel(const OverlapPartial* __restrict__ part,
+                                                           int64_t chains, int64_t K, int64_t G,
+                                                           int64_t cpr,
+                                                           const float* __restrict__ temp,
+                                                           double* __restrict__ alpha,
+                                                           double* __restrict__ law) {
+  const int64_t chain = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  if (chain >= chains) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float T = temp[chain / K];
+  const bool sampled = T > 0.0f;
+  const bool greedy = T == 0.0f;
+  double reach = 1.0;  // P(n >= j), kept by every lane
+  for (int64_t j = 0; j < G; ++j) {
+    const OverlapPartial* pr = part + (chain * G + j) * cpr;
+    double s = 0.0;
+    float tm = -INFINITY, dm = -INFINITY;
+    int32_t ti = INT_MAX, di = INT_MAX;
+    for (int64_t c = lane; c < cpr; c += kWave) {
+      const OverlapPartial q = pr[c];
+      s += q.s;
+      better_max(tm, ti, q.mt, q.it);
+      better_max(dm, di, q.md, q.id);
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      s += __shfl_xor(s, off, kWave);
+      const float otm = __shfl_xor(tm, off, kWave);
+      const int32_t oti = __shfl_xor(ti, off, kWave);
+      const float odm = __shfl_xor(dm, off, kWave);
+      const int32_t odi = __shfl_xor(di, off, kWave);
+      better_max(tm, ti, otm, oti);
+      better_max(dm, di, odm, odi);
+    }
+    const double aj = sampled ? s : greedy ? (ti == di ? 1.0 : 0.0) : double(NAN);
+    if (lane == 0) {
+      alpha[chain * G + j] = aj;
+      if (law) law[chain * (G + 1) + j] = reach * (1.0 - aj);
+    }
+    reach *= aj;
+  }
+  if (lane == 0 && law) law[chain * (G + 1) + G] = reach;
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1278,6 +1493,48 @@ bool logits_vec_ok(const void* t, const void* d, int esz, int64_t tsb, int64_t t
                    int64_t dsk, int64_t dsj) {
   return aligned16(t) && aligned16(d) && stride_ok(tsb, esz) && stride_ok(tsj, esz) &&
          stride_ok(dsb, esz) && stride_ok(dsk, esz) && stride_ok(dsj, esz);
+}
+
+// The acceptance-probability sweep: one partial per (chain, position, chunk),
+// after the counter region (which it never touches).
+size_t overlap_layout_bytes(int64_t B, int64_t K, int64_t G, int64_t V, int dtype) {
+  const int64_t vpr = (V + kVec - 1) / kVec;
+  const int64_t cv = chunk_vectors(dtype);
+  const int64_t cpr = (vpr + cv - 1) / cv;
+  return kCounterBytes +
+         align256(size_t(B) * size_t(K) * size_t(G) * size_t(cpr) * sizeof(OverlapPartial));
+}
+
+template <int DT, bool VEC>
+int64_t overlap_blocks() {
+  static std::atomic<int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, overlap_kernel<DT, VEC>,
+                                                   kStreamBlock, 0) != hipSuccess ||
+      blocks <= 0)
+    blocks = 1;
+  const int64_t n = int64_t(cus) * blocks;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int DT, bool VEC>
+void launch_overlap(const OverlapArgs& oa, int64_t units, hipStream_t st) {
+  int64_t grid = overlap_blocks<DT, VEC>();
+  const int64_t need = (units + kStreamWaves - 1) / kStreamWaves;
+  if (grid > need) grid = need;
+  hipLaunchKernelGGL((overlap_kernel<DT, VEC>), dim3(unsigned(grid)), dim3(kStreamBlock), 0, st,
+                     oa);
 }
 
 }  // namespace
@@ -1457,6 +1714,57 @@ const char* specverify_status_string(int status) {
     case SV_EHIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }
+}
+
+size_t specverify_accept_prob_workspace_size(int64_t B, int64_t K, int64_t gamma, int64_t V,
+                                             int dtype) {
+  if (check_dtype(dtype) != SV_OK || !sizes_ok(B, K, gamma, V)) return 0;
+  return overlap_layout_bytes(B, K, gamma, V, dtype);
+}
+
+int specverify_accept_prob(const void* target_logits, const void* draft_logits, int dtype,
+                           int64_t B, int64_t K, int64_t gamma, int64_t V, int64_t t_stride_b,
+                           int64_t t_stride_j, int64_t d_stride_b, int64_t d_stride_k,
+                           int64_t d_stride_j, const float* temperature, const double* lnZ_target,
+                           const double* lnZ_draft, double* alpha, double* law, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!target_logits || !draft_logits || !temperature || !lnZ_target || !lnZ_draft || !alpha)
+    return SV_EINVAL;
+  if (!sizes_ok(B, K, gamma, V)) return SV_EINVAL;
+  if (t_stride_b < 0 || t_stride_j < 0 || d_stride_b < 0 || d_stride_k < 0 || d_stride_j < 0)
+    return SV_EINVAL;
+  if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
+  int status = SV_OK;
+  if (!workspace_ok(workspace, workspace_bytes, overlap_layout_bytes(B, K, gamma, V, dtype),
+                    &status))
+    return status;
+  const int esz = esize(dtype);
+  const bool vec = logits_vec_ok(target_logits, draft_logits, esz, t_stride_b, t_stride_j,
+                                 d_stride_b, d_stride_k, d_stride_j);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  OverlapArgs oa{};
+  oa.rs = RowSet{target_logits, t_stride_b, t_stride_j, draft_logits, d_stride_b, d_stride_k,
+                 d_stride_j, B, gamma + 1, K, gamma, temperature};
+  oa.V = V;
+  oa.vpr = (V + kVec - 1) / kVec;
+  const int64_t cv = chunk_vectors(dtype);
+  oa.cpr = (oa.vpr + cv - 1) / cv;
+  oa.lnz_t = lnZ_target;
+  oa.lnz_d = lnZ_draft;
+  oa.part = reinterpret_cast<OverlapPartial*>(reinterpret_cast<char*>(workspace) + kCounterBytes);
+  const int64_t units = B * gamma * oa.cpr;
+  if (dtype == SV_BF16) {
+    if (vec) launch_overlap<SV_BF16, true>(oa, units, st);
+    else launch_overlap<SV_BF16, false>(oa, units, st);
+  } else {
+    if (vec) launch_overlap<SV_F32, true>(oa, units, st);
+    else launch_overlap<SV_F32, false>(oa, units, st);
+  }
+  const int64_t chains = B * K;
+  hipLaunchKernelGGL(alpha_law_kernel,
+                     dim3(unsigned((chains + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kBlock),
+                     0, st, oa.part, chains, K, gamma, oa.cpr, temperature, alpha, law);
+  return launch_status();
 }
 
 int specverify_version(void) { return 200; }

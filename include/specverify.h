@@ -188,6 +188,50 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
                     double* lnZ_target, double* lnZ_draft, int32_t* device_error,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of workspace that specverify_accept_prob needs for these sizes. Its
+ * chunk sums sit after the counter region of the other entry points, so one
+ * buffer of the largest size can serve all of them. Pure host function;
+ * returns 0 for sizes the library rejects.
+ */
+size_t specverify_accept_prob_workspace_size(int64_t B, int64_t K, int64_t gamma, int64_t V,
+                                             int dtype);
+
+/*
+ * Exact acceptance probability of every draft position, and the law of the
+ * accept length (FlashSpec technical summary, section 2 "Online bandit draft
+ * selection": the bandit's reward is the accepted fraction of draft tokens;
+ * Speculative Speculative Decoding technical summary, section 2,
+ * optimisation 1 "geometric fan-out": verified lengths fall off
+ * geometrically).
+ *   target_logits, draft_logits, strides, temperature: as specverify_step
+ *   lnZ_target  [B, gamma+1] double in: the normalisers that specverify_step
+ *               or specverify_normalize wrote (rows 0..gamma-1 are read;
+ *               not read for greedy rows)
+ *   lnZ_draft   [B, K, gamma] double in: likewise
+ *   alpha       [B, K, gamma] double out: sum_v min(p_j(v), q_j(v)) with
+ *               p_j = softmax(z_t[b, j] / T_b), q_j = softmax(z_d[b, k, j] / T_b),
+ *               the probability that position j accepts when its draft token
+ *               is drawn from q_j. Greedy rows (T == 0): 1 if the lowest-id
+ *               argmaxes of target row j and draft row (k, j) agree, else 0.
+ *               T < 0 or NaN: NaN.
+ *   law         [B, K, gamma+1] double out or NULL: P(n = m) =
+ *               alpha_0 ... alpha_{m-1} (1 - alpha_m) for m < gamma and
+ *               P(n = gamma) = alpha_0 ... alpha_{gamma-1}.
+ * Reads target rows 0..gamma-1 once and every draft row once (also those of
+ * greedy rows, whose argmax it needs). Precision: terms in float32 around a
+ * per-lane reference, sums in float64 (|d alpha| ~ 1e-7).
+ * Status: SV_EINVAL (null required pointer, sizes as specverify_step,
+ * negative stride), SV_EDTYPE, SV_EWORKSPACE, SV_EALIGN, SV_EHIP.
+ */
+int specverify_accept_prob(const void* target_logits, const void* draft_logits, int dtype,
+                           int64_t B, int64_t K, int64_t gamma, int64_t V,
+                           int64_t t_stride_b, int64_t t_stride_j,
+                           int64_t d_stride_b, int64_t d_stride_k, int64_t d_stride_j,
+                           const float* temperature, const double* lnZ_target,
+                           const double* lnZ_draft, double* alpha, double* law,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static host string describing a status code. */
 const char* specverify_status_string(int status);
 

@@ -27,6 +27,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"specverify_workspace_size", "specverify_normalize", "specverify_accept",
                           "specverify_residual_sample", "specverify_step",
+                          "specverify_accept_prob_workspace_size", "specverify_accept_prob",
                           "specverify_status_string", "specverify_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -100,6 +101,35 @@ def test_other_entry_points_validate_on_the_host():
     bad = list(args)
     bad[20] = None
     assert lib.specverify_residual_sample(*bad) == -3
+
+
+def test_accept_prob_validates_on_the_host():
+    lib = sv.load_library()
+    need = lib.specverify_accept_prob_workspace_size(2, 1, 4, 1000, 1)
+    assert lib.specverify_accept_prob_workspace_size(64, 1, 8, 128256, 1) > need > 0
+    assert lib.specverify_accept_prob_workspace_size(2, 1, 33, 1000, 1) == 0
+    assert lib.specverify_accept_prob_workspace_size(2, 1, 4, 1000, 7) == 0
+    # target, draft, dtype, B, K, gamma, V, 5 strides, T, lnZ_t, lnZ_d, alpha, law, ws, bytes, stream
+    args = [8, 8, 1, 2, 1, 4, 1000, 5000, 1000, 4000, 4000, 1000, 8, 8, 8, 8, None, 256, need, None]
+    for i, code in ((0, -1), (12, -1), (13, -1), (14, -1), (15, -1)):
+        bad = list(args)
+        bad[i] = None
+        assert lib.specverify_accept_prob(*bad) == code, i
+    bad = list(args)
+    bad[2] = 4
+    assert lib.specverify_accept_prob(*bad) == -2
+    bad = list(args)
+    bad[7] = -1
+    assert lib.specverify_accept_prob(*bad) == -1
+    bad = list(args)
+    bad[5] = 0
+    assert lib.specverify_accept_prob(*bad) == -1
+    bad = list(args)
+    bad[18] = need - 1
+    assert lib.specverify_accept_prob(*bad) == -3
+    bad = list(args)
+    bad[17] = 264
+    assert lib.specverify_accept_prob(*bad) == -4
 
 
 def test_binding_refuses_host_tensors():
