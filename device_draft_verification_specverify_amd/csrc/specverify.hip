@@ -1164,9 +1164,10 @@ struct OverlapArgs {
 // the K draft chunks of the same (b, j) are read against it. Since 2^x is
 // increasing, min(p, q) = 2^min(e_p, e_q) with e = (z / T - ln Z) log2(e): one
 // exp2 per pair. Each lane writes e = (z - m) k + (m k - ln Z log2 e) around its
-// own largest logit m, with the offset in float64, so the float32 exponent
-// carries no cancellation error where the terms are large; per-vector sums
-// in float32, lane sums in float64. Persistent: one workgroup per CU claiming
+// own largest logit m of that row (one m for the target, one for the draft),
+// with the offset in float64: the offset is then log2 of the lane's largest
+// term, so the float32 exponent carries no cancellation error where the terms
+// are large; per-vector sums in float32, lane sums in float64. Persistent: one workgroup per CU claiming
 // units from an LDS counter.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
@@ -1243,12 +1244,14 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
       OverlapPartial out{0.0, tm, -INFINITY, ti, INT_MAX};
       if (sampled) {
         const double l2d = a.lnz_d[chain * G + j] * kLog2eD;
-        float m = -INFINITY;
+        float mt = -INFINITY, md = -INFINITY;
 #pragma unroll
         for (int u = 0; u < CL; ++u)
 #pragma unroll
-          for (int q = 0; q < kVec; ++q)
-            m = fmaxf(m, fmaxf(vec_elem<DT>(rt[u], q), vec_elem<DT>(rd[u], q)));
+          for (int q = 0; q < kVec; ++q) {
+            mt = fmaxf(mt, vec_elem<DT>(rt[u], q));
+            md = fmaxf(md, vec_elem<DT>(rd[u], q));
+          }
         // re-read the raw words below rather than keep 128 unpacked values live
 #pragma unroll
         for (int u = 0; u < CL; ++u)
@@ -1258,18 +1261,17 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
             asm volatile("" : "+v"(rd[u].w[i]));
           }
         double sum = 0.0;
-        if (m > -INFINITY) {
-          const double mk = double(m) * k2;
-          const float at = float(mk - l2t);
-          const float ad = float(mk - l2d);
+        if (mt > -INFINITY && md > -INFINITY) {  // else p or q is 0 on every id of the lane
+          const float at = float(double(mt) * k2 - l2t);
+          const float ad = float(double(md) * k2 - l2d);
 #pragma unroll
           for (int u = 0; u < CL; ++u) {
             float sv = 0.0f;
 #pragma unroll
             for (int q = 0; q < kVec; ++q) {
               // -inf logits (and ids past V) give exp2(-inf) = 0
-              const float ep = fmaf(vec_elem<DT>(rt[u], q) - m, k2f, at);
-              const float eq = fmaf(vec_elem<DT>(rd[u], q) - m, k2f, ad);
+              const float ep = fmaf(vec_elem<DT>(rt[u], q) - mt, k2f, at);
+              const float eq = fmaf(vec_elem<DT>(rd[u], q) - md, k2f, ad);
               sv += __builtin_amdgcn_exp2f(fminf(ep, eq));
             }
             sum += double(sv);

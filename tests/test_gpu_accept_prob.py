@@ -3,8 +3,9 @@ against the fp64 oracle, through the C ABI.
 
 The normalisers fed to the entry point are the GPU step's own outputs (the
 composition a caller runs); the oracle computes everything from the logits.
-Bar: |d alpha| <= 2e-6 (float32 terms around a per-lane reference, float64
-sums, plus the step's |d ln Z| <= ~3e-7), |d P(n = m)| <= 1e-5; greedy rows exact.
+Bar: |d alpha| <= 5e-7 (float32 terms around per-lane references of each row,
+float64 sums, plus the step's |d ln Z| <= ~1.4e-7; measured <= 1.7e-7),
+|d P(n = m)| <= 1e-6; greedy rows exact.
 """
 from __future__ import annotations
 
@@ -19,8 +20,8 @@ from gpu_helpers import device, logits_to_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
-ALPHA_TOL = 2e-6
-LAW_TOL = 1e-5
+ALPHA_TOL = 5e-7
+LAW_TOL = 1e-6
 
 
 def _run(w, target=None, draft=None):
