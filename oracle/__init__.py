@@ -15,3 +15,4 @@ from .specverify import (  # noqa: F401
     ACCEPT, SAMPLE, FLAG_EPS, decode_logits, normalize_rows, accept_from_logprobs, verify,
 )
 from .acceptance import acceptance_probability, outcome_law, expected_accept_length  # noqa: F401
+from .speculation_cache import geometric_fanout, residual_topf, cache_lookup  # noqa: F401
