@@ -174,6 +174,22 @@ def per_config(names, reps: int, warmup: int, dev) -> dict:
                                 "us_p90": pct(ap, 90), "bytes_min": ap_bytes,
                                 "hbm_gbps": ap_bytes / (pct(ap, 50) * 1e-6) / 1e9}
         del aws
+        # residual top-F candidates of every outcome (geometric fan-out, 8 per outcome on
+        # average) and the cache lookup of this step's outcomes
+        fan = sv.geometric_fanout(w.gamma, 8 * (w.gamma + 1), 0.6)
+        tf = cold_times_us(lambda: sv.specverify_residual_topf(tgt, dft, temp, lz_t, lz_d, fan),
+                           reps, warmup, scratch, stream)
+        cand, _ = sv.specverify_residual_topf(tgt, dft, temp, lz_t, lz_d, fan)
+        lk = cold_times_us(lambda: sv.specverify_cache_lookup(cand, fan, plan.out.accept_len,
+                                                              plan.out.out_token),
+                           reps, warmup, scratch, stream)
+        tf_bytes = (w.B * (w.gamma + 1) * w.V + w.B * w.K * w.gamma * w.V) * w.bytes_per_logit
+        entry["residual_topf"] = {"fanout": fan, "us_median": pct(tf, 50), "us_p10": pct(tf, 10),
+                                  "us_p90": pct(tf, 90), "bytes_min": tf_bytes,
+                                  "hbm_gbps": tf_bytes / (pct(tf, 50) * 1e-6) / 1e9}
+        entry["cache_lookup"] = {"us_median": pct(lk, 50), "us_p10": pct(lk, 10),
+                                 "us_p90": pct(lk, 90)}
+        del cand
         res[name] = entry
         if name == "c4":
             # the accept test alone on this step's [B, K, gamma] log-probabilities

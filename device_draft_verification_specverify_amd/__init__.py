@@ -24,6 +24,7 @@ SV_ERR_TEMP = 2
 SV_ERR_ROW = 4
 MAX_GAMMA = 32
 MAX_CHAIN_DECISIONS = 64
+MAX_FANOUT = 64
 
 _lib = None
 
@@ -45,6 +46,10 @@ _SIGNATURES = {
     "specverify_accept_prob_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
     "specverify_accept_prob": (_INT, [_P, _P, _INT, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                       _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "specverify_geometric_fanout": (_INT, [_I64, _I64, ctypes.c_double, _P]),
+    "specverify_residual_topf": (_INT, [_P, _P, _INT, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                        _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "specverify_cache_lookup": (_INT, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "specverify_status_string": (ctypes.c_char_p, [_INT]),
     "specverify_version": (_INT, []),
 }
@@ -290,6 +295,68 @@ def specverify_accept_prob(target: torch.Tensor, draft: torch.Tensor, temperatur
         ws.numel(), _stream(dev))
     _check(st, "specverify_accept_prob")
     return alpha, law
+
+
+def _fanout_array(fanout):
+    arr = (ctypes.c_int32 * len(fanout))(*[int(f) for f in fanout])
+    return arr
+
+
+def geometric_fanout(gamma: int, total: int, ratio: float) -> list:
+    """Candidates per outcome n = 0..gamma, proportional to ratio**n, summing to total."""
+    out = (ctypes.c_int32 * (gamma + 1))()
+    _check(load_library().specverify_geometric_fanout(gamma, total, float(ratio), out),
+           "specverify_geometric_fanout")
+    return list(out)
+
+
+def specverify_residual_topf(target: torch.Tensor, draft: torch.Tensor, temperature: torch.Tensor,
+                             lnZ_target: torch.Tensor, lnZ_draft: torch.Tensor, fanout,
+                             want_weights: bool = False):
+    """cand [B, K, sum F] int32 (outcome-major, best first, -1 padding) and optionally their
+    float32 weights, for the fan-out F_0..F_gamma (a host sequence)."""
+    lib = load_library()
+    _logits(target, 3, "target")
+    _logits(draft, 4, "draft")
+    B, G1, V = target.shape
+    K, g = draft.shape[1], draft.shape[2]
+    if G1 != g + 1 or draft.shape[0] != B or draft.shape[3] != V or draft.dtype != target.dtype:
+        raise SpecVerifyError("target [B, gamma+1, V] and draft [B, K, gamma, V] disagree")
+    if len(fanout) != g + 1:
+        raise SpecVerifyError(f"fanout needs gamma + 1 = {g + 1} entries")
+    _need(temperature, torch.float32, (B,), "temperature")
+    _need(lnZ_target, torch.float64, (B, g + 1), "lnZ_target")
+    _need(lnZ_draft, torch.float64, (B, K, g), "lnZ_draft")
+    dev = target.device
+    ftot = int(sum(int(f) for f in fanout))
+    cand = torch.empty((B, K, ftot), dtype=torch.int32, device=dev)
+    w = torch.empty((B, K, ftot), dtype=torch.float32, device=dev) if want_weights else None
+    st = lib.specverify_residual_topf(
+        target.data_ptr(), draft.data_ptr(), _dtype_code(target), B, K, g, V, target.stride(0),
+        target.stride(1), draft.stride(0), draft.stride(1), draft.stride(2), temperature.data_ptr(),
+        lnZ_target.data_ptr(), lnZ_draft.data_ptr(), _fanout_array(fanout), cand.data_ptr(),
+        _ptr(w), _stream(dev))
+    _check(st, "specverify_residual_topf")
+    return cand, w
+
+
+def specverify_cache_lookup(cand: torch.Tensor, fanout, accept_len: torch.Tensor,
+                            out_token: torch.Tensor) -> torch.Tensor:
+    """slot [B, K] int32: index of out_token among the candidates of outcome accept_len, or -1."""
+    lib = load_library()
+    B, K, ftot = cand.shape
+    g = len(fanout) - 1
+    if ftot != sum(int(f) for f in fanout):
+        raise SpecVerifyError("cand's last axis must equal sum(fanout)")
+    _need(cand, torch.int32, (B, K, ftot), "cand")
+    _need(accept_len, torch.int32, (B, K), "accept_len")
+    _need(out_token, torch.int32, (B, K), "out_token")
+    slot = torch.empty((B, K), dtype=torch.int32, device=cand.device)
+    st = lib.specverify_cache_lookup(cand.data_ptr(), _fanout_array(fanout), B, K, g,
+                                     accept_len.data_ptr(), out_token.data_ptr(), slot.data_ptr(),
+                                     _stream(cand.device))
+    _check(st, "specverify_cache_lookup")
+    return slot
 
 
 def version() -> int:

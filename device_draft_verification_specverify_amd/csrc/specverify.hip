@@ -1356,6 +1356,244 @@ __global__ __launch_bounds__(kBlock) void alpha_law_kernel(const OverlapPartial*
 }
 
 // ---------------------------------------------------------------------------
+// Speculation cache: for every chain and outcome n = j, the F_j most likely
+// emitted tokens -- the largest max(p_j - q_j, 0) for j < gamma, the largest
+// p_gamma for j = gamma, the largest raw target logits for greedy rows (ties
+// to the lowest id) -- and the lookup of a step's (n, y) among them.
+
+constexpr int kTopFBlock = 256;
+constexpr int kTopFCap = 4096;                   // LDS candidate buffer (entries)
+constexpr int kTopFBatch = kTopFBlock * kVec;    // ids scored per pass of the workgroup
+
+struct TopFArgs {
+  RowSet rs;
+  int64_t V, vpr;
+  const double* lnz_t;   // [B, G+1]
+  const double* lnz_d;   // [B, K, G]
+  int32_t fan[SV_MAX_GAMMA + 1];
+  int32_t off[SV_MAX_GAMMA + 2];
+  int64_t ftot;
+  int32_t* cand;         // [B*K][ftot]
+  float* cand_w;         // [B*K][ftot] or null
+};
+
+__device__ __forceinline__ bool topf_before(float sa, int32_t ia, float sb, int32_t ib) {
+  return sa > sb || (sa == sb && ia < ib);
+}
+
+// Bitonic sort of n entries (n <= kTopFCap, padded to a power of two with
+// entries that sort last) into best-first order, by the whole workgroup.
+__device__ void topf_sort(float* sw, int32_t* si, int n) {
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  for (int i = n + int(threadIdx.x); i < n2; i += kTopFBlock) {
+    sw[i] = -INFINITY;
+    si[i] = INT_MAX;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = threadIdx.x; i < n2; i += kTopFBlock) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const bool first = (i & k) == 0;
+          const bool later_is_better = topf_before(sw[ixj], si[ixj], sw[i], si[i]);
+          if (later_is_better == first) {
+            const float tw = sw[i];
+            const int32_t ti = si[i];
+            sw[i] = sw[ixj];
+            si[i] = si[ixj];
+            sw[ixj] = tw;
+            si[ixj] = ti;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Barrier for LDS hand-offs only: global loads issued before it stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One workgroup per (chain, outcome j) with F_j > 0. A streaming selection:
+// ids whose score reaches the current threshold go to an LDS buffer; past 256
+// entries the buffer is sorted, cut to the best F_j, and the threshold becomes
+// the F_j-th score. The first threshold is the F_j-th largest of the threads'
+// maxima over the first pass (F_j distinct ids reach it, so it is no higher
+// than the row's F_j-th score). The next pass's vectors load while the
+// current one is scored. Scores: residual or target weights in float32 (the
+// exponent split in two floats so that large z/T costs no precision), raw
+// logits for greedy rows; -inf = not a candidate.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
+  __shared__ float sw[kTopFCap];
+  __shared__ int32_t si[kTopFCap];
+  __shared__ float s_max[kTopFBlock];
+  __shared__ int s_cnt;
+  __shared__ float s_thr;
+  constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  const RowSet& rs = a.rs;
+  const int64_t G = rs.G;
+  const int64_t row = blockIdx.x;
+  const int64_t chain = row / (G + 1);
+  const int j = int(row - chain * (G + 1));
+  const int F = a.fan[j];
+  if (F == 0) return;
+  const int tid = threadIdx.x;
+  const int64_t b = chain / rs.K;
+  const int64_t k = chain - b * rs.K;
+  const float T = rs.temp[b];
+  const bool sampled = T > 0.0f;
+  const bool greedy = T == 0.0f;
+  const bool residual = sampled && j < G;
+  int32_t* out = a.cand + chain * a.ftot + a.off[j];
+  float* outw = a.cand_w ? a.cand_w + chain * a.ftot + a.off[j] : nullptr;
+  if (!(sampled || greedy)) {
+    for (int i = tid; i < F; i += kTopFBlock) {
+      out[i] = -1;
+      if (outw) outw[i] = -INFINITY;
+    }
+    return;
+  }
+  const void* trow = row_ptr(rs.t, esz, b * rs.tsb + int64_t(j) * rs.tsj);
+  const void* drow = residual ? row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + int64_t(j) * rs.dsj)
+                              : trow;
+  // a2 = z k2 - ln Z log2 e as fma(z, k_hi, -c_hi) + fma(z, k_lo, -c_lo)
+  const double k2d = sampled ? kLog2eD / double(T) : 0.0;
+  const float k_hi = float(k2d);
+  const float k_lo = float(k2d - double(k_hi));
+  const double l2t = sampled ? a.lnz_t[b * (G + 1) + j] * kLog2eD : 0.0;
+  const float c_hi = float(l2t);
+  const float c_lo = float(l2t - double(c_hi));
+  const float d2 = residual ? float((a.lnz_t[b * (G + 1) + j] - a.lnz_d[chain * G + j]) * kLog2eD)
+                            : 0.0f;
+  if (tid == 0) {
+    s_cnt = 0;
+    s_thr = -INFINITY;
+  }
+  RawVec<DT> nt = neg_inf_vec<DT>(), nd = neg_inf_vec<DT>();
+  if (tid < a.vpr) {
+    nt = load_vec_bounded<DT, VEC>(trow, tid, a.V);
+    if (residual) nd = load_vec_bounded<DT, VEC>(drow, tid, a.V);
+  }
+  __syncthreads();
+  for (int64_t base = 0; base < a.vpr; base += kTopFBlock) {
+    const int64_t vi = base + tid;
+    const RawVec<DT> rt = nt;
+    const RawVec<DT> rd = nd;
+    const int64_t vn = vi + kTopFBlock;
+    if (vn < a.vpr) {
+      nt = load_vec_bounded<DT, VEC>(trow, vn, a.V);
+      if (residual) nd = load_vec_bounded<DT, VEC>(drow, vn, a.V);
+    }
+    float sc[kVec];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) {
+      const float zt = vec_elem<DT>(rt, t);
+      float score = -INFINITY;
+      if (vi < a.vpr) {
+        if (greedy) {
+          score = zt;
+        } else {
+          const float a2 = fmaf(zt, k_hi, -c_hi) + fmaf(zt, k_lo, -c_lo);
+          float w = __builtin_amdgcn_exp2f(a2);
+          if (residual) w -= __builtin_amdgcn_exp2f(a2 + fmaf(vec_elem<DT>(rd, t) - zt, k_hi, d2));
+          score = w > 0.0f ? w : -INFINITY;
+        }
+      }
+      sc[t] = score;
+      mx = fmaxf(mx, score);
+    }
+    float thr;
+    if (base == 0) {
+      // first threshold: the F-th largest of the threads' maxima (sorted, largest first)
+      s_max[tid] = mx;
+      lds_barrier();
+      for (int kk = 2; kk <= kTopFBlock; kk <<= 1) {
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+          const int ixj = tid ^ jj;
+          float mine = s_max[tid], other = s_max[ixj];
+          lds_barrier();
+          if (ixj > tid) {
+            const bool first = (tid & kk) == 0;
+            if ((other > mine) == first) {
+              s_max[tid] = other;
+              s_max[ixj] = mine;
+            }
+          }
+          lds_barrier();
+        }
+      }
+      thr = s_max[F - 1];
+    } else {
+      thr = s_thr;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int t = 0; t < kVec; ++t) {
+      const bool keep = sc[t] > -INFINITY && sc[t] >= thr;
+      sc[t] = keep ? sc[t] : -INFINITY;
+      mine += keep ? 1 : 0;
+    }
+    if (mine) {
+      int slot = atomicAdd(&s_cnt, mine);
+#pragma unroll
+      for (int t = 0; t < kVec; ++t)
+        if (sc[t] > -INFINITY) {
+          sw[slot] = sc[t];
+          si[slot] = int32_t(vi * kVec + t);
+          ++slot;
+        }
+    }
+    if (base == 0 && tid == 0) s_thr = thr;
+    lds_barrier();
+    const int cnt = s_cnt;
+    if (cnt > kTopFCap - kTopFBatch || cnt > 256) {  // cut to the best F
+      topf_sort(sw, si, cnt);
+      if (tid == 0) {
+        s_cnt = cnt < F ? cnt : F;
+        if (cnt >= F && sw[F - 1] > s_thr) s_thr = sw[F - 1];
+      }
+    }
+    lds_barrier();
+  }
+  const int cnt = s_cnt;
+  topf_sort(sw, si, cnt);
+  for (int i = tid; i < F; i += kTopFBlock) {
+    const bool have = i < cnt;
+    out[i] = have ? si[i] : -1;
+    if (outw) outw[i] = have ? sw[i] : -INFINITY;
+  }
+}
+
+// One thread per chain: the slot of the emitted token among the candidates of
+// the chain's outcome (accept length n), or -1.
+__global__ __launch_bounds__(kBlock) void cache_lookup_kernel(const int32_t* __restrict__ cand,
+                                                              TopFArgs a, int64_t chains,
+                                                              const int32_t* __restrict__ n_in,
+                                                              const int32_t* __restrict__ y_in,
+                                                              int32_t* __restrict__ slot) {
+  const int64_t chain = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  if (chain >= chains) return;
+  const int32_t n = n_in[chain];
+  const int32_t y = y_in[chain];
+  int32_t hit = -1;
+  if (n >= 0 && n <= a.rs.G && y >= 0) {
+    const int32_t* c = cand + chain * a.ftot;
+    for (int32_t i = a.off[n]; i < a.off[n + 1]; ++i)
+      if (c[i] == y) {
+        hit = i;
+        break;
+      }
+  }
+  slot[chain] = hit;
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1537,6 +1775,21 @@ void launch_overlap(const OverlapArgs& oa, int64_t units, hipStream_t st) {
   if (grid > need) grid = need;
   hipLaunchKernelGGL((overlap_kernel<DT, VEC>), dim3(unsigned(grid)), dim3(kStreamBlock), 0, st,
                      oa);
+}
+
+// Outcome fan-out (host array [G+1]) into the kernel arguments; false if any
+// entry is outside [0, SV_MAX_FANOUT].
+bool fill_fanout(const int32_t* fan, int64_t G, TopFArgs& a) {
+  int64_t off = 0;
+  for (int64_t j = 0; j <= G; ++j) {
+    if (fan[j] < 0 || fan[j] > SV_MAX_FANOUT) return false;
+    a.fan[j] = fan[j];
+    a.off[j] = int32_t(off);
+    off += fan[j];
+  }
+  a.off[G + 1] = int32_t(off);
+  a.ftot = off;
+  return true;
 }
 
 }  // namespace
@@ -1766,6 +2019,99 @@ int specverify_accept_prob(const void* target_logits, const void* draft_logits, 
   hipLaunchKernelGGL(alpha_law_kernel,
                      dim3(unsigned((chains + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kBlock),
                      0, st, oa.part, chains, K, gamma, oa.cpr, temperature, alpha, law);
+  return launch_status();
+}
+
+int specverify_geometric_fanout(int64_t gamma, int64_t total, double ratio, int32_t* fanout) {
+  if (!fanout || gamma < 1 || gamma > SV_MAX_GAMMA || total < 0 ||
+      total > (gamma + 1) * int64_t(SV_MAX_FANOUT) || !(ratio > 0.0 && ratio <= 1.0))
+    return SV_EINVAL;
+  double share[SV_MAX_GAMMA + 1], exact[SV_MAX_GAMMA + 1], sum = 0.0;
+  for (int64_t j = 0; j <= gamma; ++j) {
+    share[j] = std::pow(ratio, double(j));
+    sum += share[j];
+  }
+  int64_t used = 0;
+  double rem[SV_MAX_GAMMA + 1];
+  bool got[SV_MAX_GAMMA + 1];
+  for (int64_t j = 0; j <= gamma; ++j) {
+    exact[j] = double(total) * share[j] / sum;
+    fanout[j] = int32_t(std::floor(exact[j]));
+    rem[j] = exact[j] - double(fanout[j]);
+    got[j] = false;
+    used += fanout[j];
+  }
+  // one more to each of the largest remainders, ties to the smaller j
+  for (int64_t left = total - used; left > 0; --left) {
+    int64_t best = -1;
+    double br = -1.0;
+    for (int64_t j = 0; j <= gamma; ++j)
+      if (!got[j] && rem[j] > br) {
+        best = j;
+        br = rem[j];
+      }
+    if (best < 0) break;
+    got[best] = true;
+    fanout[best] += 1;
+  }
+  for (int64_t j = 0; j <= gamma; ++j)
+    if (fanout[j] > SV_MAX_FANOUT) return SV_EINVAL;
+  return SV_OK;
+}
+
+int specverify_residual_topf(const void* target_logits, const void* draft_logits, int dtype,
+                             int64_t B, int64_t K, int64_t gamma, int64_t V, int64_t t_stride_b,
+                             int64_t t_stride_j, int64_t d_stride_b, int64_t d_stride_k,
+                             int64_t d_stride_j, const float* temperature,
+                             const double* lnZ_target, const double* lnZ_draft,
+                             const int32_t* fanout, int32_t* cand, float* cand_weight,
+                             void* stream) {
+  if (!target_logits || !draft_logits || !temperature || !lnZ_target || !lnZ_draft || !fanout ||
+      !cand)
+    return SV_EINVAL;
+  if (!sizes_ok(B, K, gamma, V)) return SV_EINVAL;
+  if (t_stride_b < 0 || t_stride_j < 0 || d_stride_b < 0 || d_stride_k < 0 || d_stride_j < 0)
+    return SV_EINVAL;
+  if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
+  TopFArgs ta{};
+  if (!fill_fanout(fanout, gamma, ta)) return SV_EINVAL;
+  if (ta.ftot == 0) return SV_OK;
+  const int esz = esize(dtype);
+  const bool vec = logits_vec_ok(target_logits, draft_logits, esz, t_stride_b, t_stride_j,
+                                 d_stride_b, d_stride_k, d_stride_j);
+  ta.rs = RowSet{target_logits, t_stride_b, t_stride_j, draft_logits, d_stride_b, d_stride_k,
+                 d_stride_j, B, gamma + 1, K, gamma, temperature};
+  ta.V = V;
+  ta.vpr = (V + kVec - 1) / kVec;
+  ta.lnz_t = lnZ_target;
+  ta.lnz_d = lnZ_draft;
+  ta.cand = cand;
+  ta.cand_w = cand_weight;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid{unsigned(B * K * (gamma + 1)), 1u, 1u};
+  if (dtype == SV_BF16) {
+    if (vec) hipLaunchKernelGGL((topf_kernel<SV_BF16, true>), grid, dim3(kTopFBlock), 0, st, ta);
+    else hipLaunchKernelGGL((topf_kernel<SV_BF16, false>), grid, dim3(kTopFBlock), 0, st, ta);
+  } else {
+    if (vec) hipLaunchKernelGGL((topf_kernel<SV_F32, true>), grid, dim3(kTopFBlock), 0, st, ta);
+    else hipLaunchKernelGGL((topf_kernel<SV_F32, false>), grid, dim3(kTopFBlock), 0, st, ta);
+  }
+  return launch_status();
+}
+
+int specverify_cache_lookup(const int32_t* cand, const int32_t* fanout, int64_t B, int64_t K,
+                            int64_t gamma, const int32_t* accept_len, const int32_t* out_token,
+                            int32_t* slot, void* stream) {
+  if (!cand || !fanout || !accept_len || !out_token || !slot) return SV_EINVAL;
+  if (B < 1 || K < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || B > (int64_t(1) << 40) / K)
+    return SV_EINVAL;
+  TopFArgs ta{};
+  if (!fill_fanout(fanout, gamma, ta)) return SV_EINVAL;
+  ta.rs.G = gamma;
+  const int64_t chains = B * K;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(cache_lookup_kernel, dim3(unsigned((chains + kBlock - 1) / kBlock)),
+                     dim3(kBlock), 0, st, cand, ta, chains, accept_len, out_token, slot);
   return launch_status();
 }
 

@@ -81,6 +81,7 @@ extern "C" {
 /* Size limits checked on the host. */
 #define SV_MAX_GAMMA 32
 #define SV_MAX_CHAIN_DECISIONS 64 /* K * gamma per batch row */
+#define SV_MAX_FANOUT 64          /* candidates per verification outcome */
 
 /*
  * Bytes of workspace that specverify_step / specverify_normalize /
@@ -231,6 +232,65 @@ int specverify_accept_prob(const void* target_logits, const void* draft_logits, 
                            const float* temperature, const double* lnZ_target,
                            const double* lnZ_draft, double* alpha, double* law,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Speculation-cache fan-out (Speculative Speculative Decoding technical
+ * summary, section 2, optimisation 1 "geometric fan-out": verified lengths
+ * fall off geometrically, so short accept lengths get more candidates).
+ * Pure host function. fanout [gamma+1] int32 HOST out: F_j proportional to
+ * ratio^j, rounded to integers summing to `total` by largest remainders (ties
+ * to the smaller j). Status: SV_EINVAL (null, gamma outside [1, 32], ratio
+ * outside (0, 1], total < 0 or an F_j above SV_MAX_FANOUT).
+ */
+int specverify_geometric_fanout(int64_t gamma, int64_t total, double ratio, int32_t* fanout);
+
+/*
+ * The most likely emitted tokens of every verification outcome (Speculative
+ * Speculative Decoding technical summary, core mechanism items 2-3: a cache
+ * keyed by the outcome -- how many drafts are accepted and which token
+ * follows; section 2, optimisation 2: that token is drawn from the residual
+ * max(p_target - p_draft, 0)).
+ *   target_logits, draft_logits, strides, temperature, lnZ_target,
+ *   lnZ_draft: as specverify_accept_prob
+ *   fanout      [gamma+1] int32 HOST: F_j candidates for outcome n = j, each
+ *               in [0, SV_MAX_FANOUT]
+ *   cand        [B, K, sum F] int32 out, outcome-major: for outcome j < gamma
+ *               the F_j ids of largest max(p_j - q_j, 0); for j = gamma those of
+ *               largest p_gamma; greedy rows (T == 0): those of largest raw
+ *               target logit of row j. Best first, ties to the lowest id; ids
+ *               of zero weight (-inf logit for greedy rows) are never listed,
+ *               so a short support is padded with -1. T < 0 or NaN: all -1.
+ *   cand_weight [B, K, sum F] float out or NULL: the candidates' weights
+ *               (r_j or p_gamma; raw logits for greedy rows), -inf for padding.
+ * Weights are ranked in float32 (relative error ~1e-6), so ids whose weights
+ * differ by less than that may swap places. No workspace.
+ * Status: SV_EINVAL (null required pointer, sizes as specverify_step, a
+ * fan-out entry outside [0, SV_MAX_FANOUT], negative stride), SV_EDTYPE,
+ * SV_EHIP.
+ */
+int specverify_residual_topf(const void* target_logits, const void* draft_logits, int dtype,
+                             int64_t B, int64_t K, int64_t gamma, int64_t V,
+                             int64_t t_stride_b, int64_t t_stride_j,
+                             int64_t d_stride_b, int64_t d_stride_k, int64_t d_stride_j,
+                             const float* temperature, const double* lnZ_target,
+                             const double* lnZ_draft, const int32_t* fanout, int32_t* cand,
+                             float* cand_weight, void* stream);
+
+/*
+ * Cache hit test of a step's outcome (same passage, item 3: a hit returns the
+ * prepared continuation at once).
+ *   cand        [B, K, sum F] int32 from specverify_residual_topf
+ *   fanout      [gamma+1] int32 HOST, as given there
+ *   accept_len, out_token [B, K] int32 from specverify_step
+ *   slot        [B, K] int32 out: index into cand[b, k, :] of out_token among
+ *               the candidates of outcome n = accept_len, or -1 (miss, or
+ *               n outside [0, gamma], or a negative token).
+ * Status: SV_EINVAL (null pointer, B/K < 1, gamma outside [1, 32], a fan-out
+ * entry outside [0, SV_MAX_FANOUT]), SV_EHIP.
+ */
+int specverify_cache_lookup(const int32_t* cand, const int32_t* fanout, int64_t B, int64_t K,
+                            int64_t gamma, const int32_t* accept_len, const int32_t* out_token,
+                            int32_t* slot, void* stream);
 
 /* Static host string describing a status code. */
 const char* specverify_status_string(int status);

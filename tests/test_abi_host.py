@@ -28,6 +28,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"specverify_workspace_size", "specverify_normalize", "specverify_accept",
                           "specverify_residual_sample", "specverify_step",
                           "specverify_accept_prob_workspace_size", "specverify_accept_prob",
+                          "specverify_geometric_fanout", "specverify_residual_topf",
+                          "specverify_cache_lookup",
                           "specverify_status_string", "specverify_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -130,6 +132,53 @@ def test_accept_prob_validates_on_the_host():
     bad = list(args)
     bad[17] = 264
     assert lib.specverify_accept_prob(*bad) == -4
+
+
+def test_geometric_fanout_matches_the_oracle():
+    # a pure host function: checked against the oracle here, without a GPU
+    import oracle
+    for g, tot, a in ((2, 7, 0.5), (2, 10, 0.5), (3, 6, 1.0), (8, 64, 0.6), (4, 33, 0.9),
+                      (1, 5, 0.2), (32, 300, 0.85), (8, 0, 0.5), (5, 384, 1.0)):
+        assert sv.geometric_fanout(g, tot, a) == oracle.geometric_fanout(g, tot, a).tolist(), (g, tot, a)
+    lib = sv.load_library()
+    import ctypes
+    out = (ctypes.c_int32 * 40)()
+    assert lib.specverify_geometric_fanout(2, 10, 0.0, out) == -1
+    assert lib.specverify_geometric_fanout(2, 10, 1.5, out) == -1
+    assert lib.specverify_geometric_fanout(33, 10, 0.5, out) == -1
+    assert lib.specverify_geometric_fanout(2, 3 * 64 + 1, 1.0, out) == -1
+    assert lib.specverify_geometric_fanout(2, 10, 0.5, None) == -1
+
+
+def test_topf_and_lookup_validate_on_the_host():
+    import ctypes
+    lib = sv.load_library()
+    fan = (ctypes.c_int32 * 5)(4, 3, 2, 1, 1)
+    args = [8, 8, 1, 2, 1, 4, 1000, 5000, 1000, 4000, 4000, 1000, 8, 8, 8, fan, 8, None, None]
+    for i in (0, 12, 13, 14, 15, 16):
+        bad = list(args)
+        bad[i] = None
+        assert lib.specverify_residual_topf(*bad) == -1, i
+    bad = list(args)
+    bad[2] = 7
+    assert lib.specverify_residual_topf(*bad) == -2
+    bad = list(args)
+    bad[15] = (ctypes.c_int32 * 5)(4, 65, 2, 1, 1)
+    assert lib.specverify_residual_topf(*bad) == -1
+    bad = list(args)
+    bad[15] = (ctypes.c_int32 * 5)(4, -1, 2, 1, 1)
+    assert lib.specverify_residual_topf(*bad) == -1
+    bad = list(args)
+    bad[10] = -3
+    assert lib.specverify_residual_topf(*bad) == -1
+    largs = [8, fan, 2, 1, 4, 8, 8, 8, None]
+    for i in (0, 1, 5, 6, 7):
+        bad = list(largs)
+        bad[i] = None
+        assert lib.specverify_cache_lookup(*bad) == -1, i
+    bad = list(largs)
+    bad[4] = 0
+    assert lib.specverify_cache_lookup(*bad) == -1
 
 
 def test_binding_refuses_host_tensors():
