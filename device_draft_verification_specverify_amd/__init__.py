@@ -50,6 +50,12 @@ _SIGNATURES = {
     "specverify_residual_topf": (_INT, [_P, _P, _INT, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                         _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "specverify_cache_lookup": (_INT, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "specverify_bandit_state_size": (_SZ, [ctypes.c_int32]),
+    "specverify_bandit_init": (_INT, [_P, _SZ, ctypes.c_int32, ctypes.c_int32, _U64, ctypes.c_double]),
+    "specverify_bandit_select": (_INT, [_P, _P]),
+    "specverify_bandit_update": (_INT, [_P, ctypes.c_int32, ctypes.c_double]),
+    "specverify_bandit_stats": (_INT, [_P, ctypes.c_int32, _P, _P]),
+    "specverify_step_reward": (_INT, [_P, _I64, _I64, _P]),
     "specverify_status_string": (ctypes.c_char_p, [_INT]),
     "specverify_version": (_INT, []),
 }
@@ -357,6 +363,54 @@ def specverify_cache_lookup(cand: torch.Tensor, fanout, accept_len: torch.Tensor
                                      _stream(cand.device))
     _check(st, "specverify_cache_lookup")
     return slot
+
+
+BANDIT_UCB1 = 0
+BANDIT_THOMPSON = 1
+
+
+class Bandit:
+    """Draft selector between steps (host only): UCB1 or Thompson sampling over `arms`
+    draft models, rewarded with the accepted fraction of each step's draft tokens."""
+
+    def __init__(self, arms: int, policy: int = BANDIT_UCB1, seed: int = 0, c: float = 2.0):
+        lib = load_library()
+        n = int(lib.specverify_bandit_state_size(arms))
+        if n == 0:
+            raise SpecVerifyError(f"arms must be in [1, 256], got {arms}")
+        self._lib = lib
+        self._state = ctypes.create_string_buffer(n)
+        _check(lib.specverify_bandit_init(self._state, n, arms, policy, seed & (2 ** 64 - 1),
+                                          float(c)), "specverify_bandit_init")
+        self.arms = arms
+
+    def select(self) -> int:
+        arm = ctypes.c_int32()
+        _check(self._lib.specverify_bandit_select(self._state, ctypes.byref(arm)),
+               "specverify_bandit_select")
+        return arm.value
+
+    def update(self, arm: int, reward: float) -> None:
+        _check(self._lib.specverify_bandit_update(self._state, arm, float(reward)),
+               "specverify_bandit_update")
+
+    def stats(self, arm: int) -> tuple:
+        pulls, total = ctypes.c_int64(), ctypes.c_double()
+        _check(self._lib.specverify_bandit_stats(self._state, arm, ctypes.byref(pulls),
+                                                 ctypes.byref(total)), "specverify_bandit_stats")
+        return pulls.value, total.value
+
+
+def step_reward(accept_len, gamma: int) -> float:
+    """Accepted fraction of a step's draft tokens from its accept lengths (any host array
+    or tensor; a device tensor is copied to the host)."""
+    if isinstance(accept_len, torch.Tensor):
+        accept_len = accept_len.detach().to("cpu")
+    arr = torch.as_tensor(accept_len, dtype=torch.int32).contiguous().reshape(-1)
+    out = ctypes.c_double()
+    _check(load_library().specverify_step_reward(arr.data_ptr(), arr.numel(), gamma,
+                                                  ctypes.byref(out)), "specverify_step_reward")
+    return out.value
 
 
 def version() -> int:

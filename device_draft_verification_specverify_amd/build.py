@@ -12,6 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCE = os.path.join(HERE, "csrc", "specverify.hip")
+HOST_SOURCES = [os.path.join(HERE, "csrc", "bandit.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libspecverify.so")
 ARCH = "gfx950"
@@ -40,7 +41,8 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     """Compile the HIP source into LIBRARY (always recompiles). Returns the path."""
     tmp = LIBRARY + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, SOURCE, "-o", tmp]
+    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, SOURCE, *HOST_SOURCES,
+           "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -82,6 +82,11 @@ extern "C" {
 #define SV_MAX_GAMMA 32
 #define SV_MAX_CHAIN_DECISIONS 64 /* K * gamma per batch row */
 #define SV_MAX_FANOUT 64          /* candidates per verification outcome */
+#define SV_MAX_ARMS 256           /* draft models of the bandit selector */
+
+/* Bandit policies (specverify_bandit_init). */
+#define SV_BANDIT_UCB1 0
+#define SV_BANDIT_THOMPSON 1
 
 /*
  * Bytes of workspace that specverify_step / specverify_normalize /
@@ -291,6 +296,41 @@ int specverify_residual_topf(const void* target_logits, const void* draft_logits
 int specverify_cache_lookup(const int32_t* cand, const int32_t* fanout, int64_t B, int64_t K,
                             int64_t gamma, const int32_t* accept_len, const int32_t* out_token,
                             int32_t* slot, void* stream);
+
+/*
+ * Draft selection between decoding steps (FlashSpec technical summary,
+ * section 2 "Online bandit draft selection": a K-armed bandit over draft
+ * models whose reward is the accepted fraction of draft tokens, with UCB1 or
+ * Thompson sampling; the policy sees only past acceptance, so the verified
+ * output distribution is unchanged). HOST functions on a HOST state buffer the
+ * caller owns; no GPU work, no allocation, not thread-safe per state.
+ *
+ * specverify_bandit_state_size: bytes of state for `arms` arms (0 if arms is
+ *   outside [1, SV_MAX_ARMS]).
+ * specverify_bandit_init: policy SV_BANDIT_UCB1 (Auer, Cesa-Bianchi, Fischer
+ *   2002: each arm once in index order, then argmax mean_i + sqrt(c ln t / n_i),
+ *   t = rewards so far, c = 2 in the paper) or SV_BANDIT_THOMPSON (argmax of
+ *   theta_i ~ Beta(1 + S_i, 1 + n_i - S_i), S_i the arm's reward sum; Beta draws
+ *   from two Marsaglia-Tsang Gamma variates on uniforms of Philox4x32-10 keyed
+ *   by `seed`, counter (draw, arm, (variate << 16) | attempt, 2)). Ties go to the
+ *   lowest index. Status: SV_EINVAL (null, arms out of range, unknown policy,
+ *   c <= 0 or not finite), SV_EWORKSPACE (state_bytes too small).
+ * specverify_bandit_select: writes the arm for the next step.
+ * specverify_bandit_update: reward in [0, 1] for the arm just played.
+ * specverify_bandit_stats: pulls and reward sum of one arm (either may be NULL).
+ * specverify_step_reward: the reward of a step from its accept lengths (HOST
+ *   array of `chains` int32): sum(clamp(n, 0, gamma)) / (chains * gamma).
+ * Status of the last four: SV_EINVAL for a null or uninitialised state, an arm
+ * out of range, a reward outside [0, 1], chains < 1 or gamma outside [1, 32].
+ */
+size_t specverify_bandit_state_size(int32_t arms);
+int specverify_bandit_init(void* state, size_t state_bytes, int32_t arms, int32_t policy,
+                           uint64_t seed, double c);
+int specverify_bandit_select(void* state, int32_t* arm);
+int specverify_bandit_update(void* state, int32_t arm, double reward);
+int specverify_bandit_stats(const void* state, int32_t arm, int64_t* pulls, double* reward_sum);
+int specverify_step_reward(const int32_t* accept_len, int64_t chains, int64_t gamma,
+                           double* reward);
 
 /* Static host string describing a status code. */
 const char* specverify_status_string(int status);

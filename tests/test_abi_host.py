@@ -30,6 +30,9 @@ def test_exports_every_declared_symbol():
                           "specverify_accept_prob_workspace_size", "specverify_accept_prob",
                           "specverify_geometric_fanout", "specverify_residual_topf",
                           "specverify_cache_lookup",
+                          "specverify_bandit_state_size", "specverify_bandit_init",
+                          "specverify_bandit_select", "specverify_bandit_update",
+                          "specverify_bandit_stats", "specverify_step_reward",
                           "specverify_status_string", "specverify_version"}
     for n in names:
         assert hasattr(lib, n), n

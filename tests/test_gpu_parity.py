@@ -255,3 +255,33 @@ def test_workspace_reused_across_shapes_and_calls():
         first = first or cur
         assert np.array_equal(cur[0], first[0]) and np.array_equal(cur[1], first[1])
     assert int(plan.out.device_error.item()) == 0
+
+
+def test_bandit_loop_over_draft_models_on_the_gpu():
+    # three draft models of the same target (noise 0.3, 1.0, 2.5): a UCB1 loop of GPU
+    # steps, rewarded with each step's accepted fraction, settles on the closest draft
+    import workloads.synth as synth
+    print("[case] bandit loop, 3 draft models, 60 steps", flush=True)
+    base = workloads.make("c2", B=8, V=4000)
+    rng = np.random.default_rng(0)
+    zt = oracle.decode_logits(base.target, "bf16")
+    dev = device()
+    target = logits_to_dev(base.target, "bf16")
+    temp = to_dev(base.temperature)
+    models = []
+    for sigma in (0.3, 1.0, 2.5):
+        zd = zt[:, None, :-1] + rng.normal(0, sigma, size=base.draft.shape)
+        models.append(logits_to_dev(synth._store(zd, "bf16"), "bf16"))
+    bandit = sv.Bandit(3, sv.BANDIT_UCB1)
+    picks = []
+    for step in range(60):
+        arm = bandit.select()
+        draft = models[arm]
+        # draft tokens: the draft model's own argmax, so every arm proposes its best guess
+        toks = draft.float().argmax(dim=-1).to(torch.int32).contiguous()
+        out = sv.specverify_step(target, draft, toks, temp, 1000 + step, to_dev(base.pos0))
+        bandit.update(arm, sv.step_reward(out.accept_len, base.gamma))
+        picks.append(arm)
+    counts = np.bincount(picks, minlength=3)
+    print(f"[parity] bandit picks {counts.tolist()}", flush=True)
+    assert counts[0] > counts[1] and counts[0] > counts[2]
