@@ -831,7 +831,7 @@ __global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   __shared__ double s_lnz[kMaxRowsPerChain];
   __shared__ int32_t s_amax[SV_MAX_GAMMA + 1];
-  __shared__ int32_t s_bad;
+  __shared__ int32_t s_rowbad[kAcceptWaves];
   __shared__ int32_t s_n;
   const RowSet& rs = a.rs;
   const int64_t chain = blockIdx.x;
@@ -858,52 +858,53 @@ __global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
     __syncthreads();
     if (greedy && t == 0 && s_n >= 0) a.out_token[chain] = s_amax[s_n];
   } else {
-    // Loads that do not depend on the normalisers go first so their latency
-    // overlaps the merges: draft tokens, the logits at them, accept uniforms.
+    // The merges of the chain's rows (target rows 0..G, then draft rows
+    // (k, 0..G-1) when sampled) go first: wavefront w merges rows w, w + W
+    // (W wavefronts), the partial loads of both rows in flight together. The
+    // draft tokens are loaded before them and the logits at the tokens after
+    // the partials arrive, so those round trips overlap the reductions.
+    const int wv = t / kWave;
     int32_t x = 0;
     bool tok_bad = false;
-    float zt = 0.0f, zd = 0.0f;
-    double log_u = 0.0;
     if (t < G) {
       x = a.tokens[chain * G + t];
       tok_bad = x < 0 || int64_t(x) >= a.V;
-      if (!tok_bad && sampled) {
-        zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + t * rs.tsj), x);
-        zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + t * rs.dsj), x);
-      }
-      const uint64_t pos = uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(t);
-      const Philox4 r = philox4x32_10(0u, uint32_t(pos), uint32_t(chain), kPurposeAccept,
-                                      uint32_t(a.seed), uint32_t(a.seed >> 32));
-      log_u = log_uniform_d(unit_uniform_d(r.w[0]));
     }
-    if (t == 0) s_bad = 0;
-    if (t >= P && t < P + G) s_lnz[t] = NAN;  // stays NaN for a greedy row's drafts
-    __syncthreads();
-    // normalisers of the chain's rows (target rows 0..G, then draft rows
-    // (k, 0..G-1) when sampled): wavefront w merges rows w, w + W, w + 2W
-    // (W wavefronts), with all their partial loads issued together
-    {
-      const int nr = P + (sampled ? G : 0);
-      const int wv = t / kWave;
-      for (int base = wv; base < nr; base += kAcceptRows * kAcceptWaves) {
-        int64_t rho[kAcceptRows];
+    const int nr = P + (sampled ? G : 0);
+    int32_t row_bad = 0;
+    float zt = 0.0f, zd = 0.0f;
+    double log_u = 0.0;
+    for (int base = wv; base < nr || base == wv; base += kAcceptRows * kAcceptWaves) {
+      int64_t rho[kAcceptRows];
 #pragma unroll
-        for (int r = 0; r < kAcceptRows; ++r) {
-          const int ri = base + kAcceptWaves * r;
-          rho[r] = ri >= nr ? -1 : ri < P ? b * P + ri : rs.B * P + chain * G + (ri - P);
+      for (int r = 0; r < kAcceptRows; ++r) {
+        const int ri = base + kAcceptWaves * r;
+        rho[r] = ri >= nr ? -1 : ri < P ? b * P + ri : rs.B * P + chain * G + (ri - P);
+      }
+      float m[kAcceptRows];
+      int32_t idx[kAcceptRows];
+      double s[kAcceptRows];
+      lane_fold<kAcceptRows>(a.part, rho, a.cpr, T, m, idx, s);
+      if (base == wv && t < G) {
+        // wavefront 0: the logits at the draft tokens and the accept uniforms
+        if (!tok_bad && sampled) {
+          zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + t * rs.tsj), x);
+          zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + t * rs.dsj), x);
         }
-        float m[kAcceptRows];
-        int32_t idx[kAcceptRows];
-        double s[kAcceptRows];
-        lane_fold<kAcceptRows>(a.part, rho, a.cpr, T, m, idx, s);
-        // rows one at a time through a shifting window (rolled: less code)
+        const uint64_t pos = uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(t);
+        const Philox4 r = philox4x32_10(0u, uint32_t(pos), uint32_t(chain), kPurposeAccept,
+                                        uint32_t(a.seed), uint32_t(a.seed >> 32));
+        log_u = log_uniform_d(unit_uniform_d(r.w[0]));
+      }
+      // rows one at a time through a shifting window (rolled: less code)
 #pragma unroll 1
-        for (int r = 0; r < kAcceptRows; ++r) {
+      for (int r = 0; r < kAcceptRows; ++r) {
+        const int ri = base + kAcceptWaves * r;
+        if (ri < nr) {  // uniform across the wavefront
           const RowStat st = wave_reduce_row(m[0], idx[0], s[0], T);
-          const int ri = base + kAcceptWaves * r;
-          if (lane == 0 && ri < nr) {
+          if (lane == 0) {
             s_lnz[ri] = st.lnz;
-            if (!(st.m > -INFINITY)) atomicOr(&s_bad, SV_ERR_ROW);
+            if (!(st.m > -INFINITY)) row_bad = SV_ERR_ROW;
             if (ri < P) {
               s_amax[ri] = st.idx == INT_MAX ? 0 : st.idx;
               if (k == 0 && a.lnz_t_out) a.lnz_t_out[b * P + ri] = st.lnz;
@@ -911,15 +912,16 @@ __global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
               a.lnz_d_out[chain * G + (ri - P)] = st.lnz;
             }
           }
+        }
 #pragma unroll
-          for (int q = 0; q + 1 < kAcceptRows; ++q) {
-            m[q] = m[q + 1];
-            idx[q] = idx[q + 1];
-            s[q] = s[q + 1];
-          }
+        for (int q = 0; q + 1 < kAcceptRows; ++q) {
+          m[q] = m[q + 1];
+          idx[q] = idx[q + 1];
+          s[q] = s[q + 1];
         }
       }
     }
+    if (lane == 0) s_rowbad[wv] = row_bad;
     __syncthreads();
     // accept tests of the G positions in wavefront 0, first rejection by ballot
     if (t < kWave) {
@@ -945,7 +947,8 @@ __global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
       const uint64_t bad_mask = __ballot(tok_bad);
       if (t == 0) {
         const int n = __builtin_ctzll(~acc_mask);  // leading accepts (<= G: bit G of ~mask is set)
-        int32_t err = s_bad;
+        int32_t err = 0;
+        for (int w = 0; w < kAcceptWaves; ++w) err |= s_rowbad[w];
         if (bad_mask) err |= SV_ERR_TOKEN;
         if (!(sampled || greedy)) err |= SV_ERR_TEMP;
         s_n = err ? -1 : n;
@@ -967,7 +970,7 @@ __global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
     ChainInfo ci;
     ci.n = (n >= 0 && sampled) ? n : -1;
     ci.lzt = n >= 0 ? s_lnz[n] : 0.0;
-    ci.lzd = (n >= 0 && n < G) ? s_lnz[P + n] : 0.0;
+    ci.lzd = (n >= 0 && n < G && sampled) ? s_lnz[P + n] : 0.0;
     ci.pad[0] = ci.pad[1] = ci.pad[2] = 0;
     a.info[chain] = ci;
   }
