@@ -56,6 +56,8 @@ _SIGNATURES = {
     "specverify_bandit_update": (_INT, [_P, ctypes.c_int32, ctypes.c_double]),
     "specverify_bandit_stats": (_INT, [_P, ctypes.c_int32, _P, _P]),
     "specverify_step_reward": (_INT, [_P, _I64, _I64, _P]),
+    "specverify_branch_prune": (_INT, [_P, _I64, _I64, _I64, ctypes.c_double, _I64, _P, _P, _P,
+                                       _P]),
     "specverify_status_string": (ctypes.c_char_p, [_INT]),
     "specverify_version": (_INT, []),
 }
@@ -363,6 +365,22 @@ def specverify_cache_lookup(cand: torch.Tensor, fanout, accept_len: torch.Tensor
                                      _stream(cand.device))
     _check(st, "specverify_cache_lookup")
     return slot
+
+
+def specverify_branch_prune(logq: torch.Tensor, log_tau: float, keep: int):
+    """(keep_mask [B, K] int32, prefix_len [B, K] int32, conf [B, K, gamma] float64) from the
+    draft log-probabilities at the drafted tokens, logq [B, K, gamma] float32."""
+    B, K, g = logq.shape
+    _need(logq, torch.float32, (B, K, g), "logq")
+    dev = logq.device
+    mask = torch.empty((B, K), dtype=torch.int32, device=dev)
+    plen = torch.empty((B, K), dtype=torch.int32, device=dev)
+    conf = torch.empty((B, K, g), dtype=torch.float64, device=dev)
+    st = load_library().specverify_branch_prune(logq.data_ptr(), B, K, g, float(log_tau), keep,
+                                                mask.data_ptr(), plen.data_ptr(), conf.data_ptr(),
+                                                _stream(dev))
+    _check(st, "specverify_branch_prune")
+    return mask, plen, conf
 
 
 BANDIT_UCB1 = 0

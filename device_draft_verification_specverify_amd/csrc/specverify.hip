@@ -1597,6 +1597,51 @@ __global__ __launch_bounds__(kBlock) void cache_lookup_kernel(const int32_t* __r
 }
 
 // ---------------------------------------------------------------------------
+// Branch pruning before verification: per branch, the running sum of ln q over
+// the draft positions (float64, in order), the confident prefix L (positions
+// whose running sum is >= ln tau) and, per batch row, the `keep` branches of
+// largest L (ties: larger sum over the prefix, then lower k). One thread per
+// batch row.
+__global__ __launch_bounds__(kBlock) void branch_prune_kernel(const float* __restrict__ logq,
+                                                              int64_t B, int64_t K, int64_t G,
+                                                              double log_tau, int64_t keep,
+                                                              int32_t* __restrict__ keep_mask,
+                                                              int32_t* __restrict__ prefix_len,
+                                                              double* __restrict__ conf) {
+  const int64_t b = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  if (b >= B) return;
+  int32_t len[SV_MAX_CHAIN_DECISIONS];
+  double last[SV_MAX_CHAIN_DECISIONS];
+  for (int64_t k = 0; k < K; ++k) {
+    double c = 0.0;
+    int32_t L = 0;
+    double at = -INFINITY;
+    for (int64_t j = 0; j < G; ++j) {
+      c += double(logq[(b * K + k) * G + j]);
+      if (conf) conf[(b * K + k) * G + j] = c;
+      if (c >= log_tau) {
+        ++L;
+        at = c;
+      }
+    }
+    len[k] = L;
+    last[k] = at;
+  }
+  for (int64_t k = 0; k < K; ++k) {
+    // rank of branch k: branches ordered before it
+    int64_t ahead = 0;
+    for (int64_t o = 0; o < K; ++o) {
+      if (o == k) continue;
+      const bool before = len[o] > len[k] || (len[o] == len[k] && last[o] > last[k]) ||
+                          (len[o] == len[k] && last[o] == last[k] && o < k);
+      ahead += before ? 1 : 0;
+    }
+    keep_mask[b * K + k] = ahead < keep ? 1 : 0;
+    if (prefix_len) prefix_len[b * K + k] = len[k];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -2115,6 +2160,19 @@ int specverify_cache_lookup(const int32_t* cand, const int32_t* fanout, int64_t 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(cache_lookup_kernel, dim3(unsigned((chains + kBlock - 1) / kBlock)),
                      dim3(kBlock), 0, st, cand, ta, chains, accept_len, out_token, slot);
+  return launch_status();
+}
+
+int specverify_branch_prune(const float* logq, int64_t B, int64_t K, int64_t gamma,
+                            double log_tau, int64_t keep, int32_t* keep_mask,
+                            int32_t* prefix_len, double* conf, void* stream) {
+  if (!logq || !keep_mask || B < 1 || K < 1 || gamma < 1 || gamma > SV_MAX_GAMMA ||
+      K * gamma > SV_MAX_CHAIN_DECISIONS || keep < 0 || std::isnan(log_tau) ||
+      B > (int64_t(1) << 40))
+    return SV_EINVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(branch_prune_kernel, dim3(unsigned((B + kBlock - 1) / kBlock)), dim3(kBlock),
+                     0, st, logq, B, K, gamma, log_tau, keep, keep_mask, prefix_len, conf);
   return launch_status();
 }
 

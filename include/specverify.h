@@ -332,6 +332,27 @@ int specverify_bandit_stats(const void* state, int32_t arm, int64_t* pulls, doub
 int specverify_step_reward(const int32_t* accept_len, int64_t chains, int64_t gamma,
                            double* reward);
 
+/*
+ * Branch pruning before verification (FlexDraft technical summary,
+ * methodology component 3 "Flex decoding", selective verification for small
+ * batches: the cumulative draft confidence estimates how far each branch will
+ * be accepted; low-confidence branches are dropped and only high-confidence
+ * prefixes verified). The pages give no rule; the one taken here:
+ *   logq        [B, K, gamma] float: ln q at each branch's drafted tokens
+ *   conf        [B, K, gamma] double out or NULL: running sums of ln q over
+ *               j = 0..gamma-1, in order, in float64
+ *   prefix_len  [B, K] int32 out or NULL: positions with conf >= log_tau (a
+ *               leading run, since ln q <= 0)
+ *   keep_mask   [B, K] int32 out: 1 for the `keep` branches of each row with
+ *               the largest prefix_len (ties: larger conf at the prefix's last
+ *               position, -inf for an empty prefix; then lower k), else 0.
+ * Status: SV_EINVAL (null logq/keep_mask, B/K < 1, gamma outside [1, 32],
+ * K * gamma > 64, keep < 0, log_tau NaN), SV_EHIP.
+ */
+int specverify_branch_prune(const float* logq, int64_t B, int64_t K, int64_t gamma,
+                            double log_tau, int64_t keep, int32_t* keep_mask,
+                            int32_t* prefix_len, double* conf, void* stream);
+
 /* Static host string describing a status code. */
 const char* specverify_status_string(int status);
 

@@ -17,3 +17,4 @@ from .specverify import (  # noqa: F401
 from .acceptance import acceptance_probability, outcome_law, expected_accept_length  # noqa: F401
 from .speculation_cache import geometric_fanout, residual_topf, cache_lookup  # noqa: F401
 from . import bandit  # noqa: F401
+from . import branch_pruning  # noqa: F401

@@ -33,6 +33,7 @@ def test_exports_every_declared_symbol():
                           "specverify_bandit_state_size", "specverify_bandit_init",
                           "specverify_bandit_select", "specverify_bandit_update",
                           "specverify_bandit_stats", "specverify_step_reward",
+                          "specverify_branch_prune",
                           "specverify_status_string", "specverify_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -182,6 +183,21 @@ def test_topf_and_lookup_validate_on_the_host():
     bad = list(largs)
     bad[4] = 0
     assert lib.specverify_cache_lookup(*bad) == -1
+
+
+def test_branch_prune_validates_on_the_host():
+    lib = sv.load_library()
+    args = [8, 4, 2, 8, -1.0, 1, 8, None, None, None]
+    bad = list(args); bad[0] = None
+    assert lib.specverify_branch_prune(*bad) == -1
+    bad = list(args); bad[6] = None
+    assert lib.specverify_branch_prune(*bad) == -1
+    bad = list(args); bad[2] = 9            # K * gamma > 64
+    assert lib.specverify_branch_prune(*bad) == -1
+    bad = list(args); bad[5] = -1
+    assert lib.specverify_branch_prune(*bad) == -1
+    bad = list(args); bad[4] = float("nan")
+    assert lib.specverify_branch_prune(*bad) == -1
 
 
 def test_binding_refuses_host_tensors():

@@ -285,3 +285,20 @@ def test_bandit_loop_over_draft_models_on_the_gpu():
     counts = np.bincount(picks, minlength=3)
     print(f"[parity] bandit picks {counts.tolist()}", flush=True)
     assert counts[0] > counts[1] and counts[0] > counts[2]
+
+
+def test_branch_prune_matches_the_oracle():
+    # the pages give no rule (parity unpinned to them); the GPU must reproduce the
+    # oracle's reading exactly: float64 running sums in order, integer ranks
+    from oracle import branch_pruning as bp
+    rng = np.random.default_rng(12)
+    for B, K, g, tau, keep in ((37, 4, 8, 0.05, 2), (300, 8, 8, 0.2, 3), (5, 2, 32, 1e-3, 1),
+                               (9, 16, 4, 0.5, 16), (3, 3, 3, 0.9, 0)):
+        logq = (-rng.exponential(0.6, size=(B, K, g))).astype(np.float32)
+        logq[0, 0, :] = logq[0, 1, :]                       # an exact tie between branches
+        print(f"[case] branch prune B={B} K={K} gamma={g} tau={tau} keep={keep}", flush=True)
+        mask, plen, conf = sv.specverify_branch_prune(to_dev(logq), float(np.log(tau)), keep)
+        m_ref, l_ref, c_ref = bp.keep_branches(logq, float(np.log(tau)), keep)
+        assert np.array_equal(conf.cpu().numpy(), c_ref)
+        assert np.array_equal(plen.cpu().numpy(), l_ref)
+        assert np.array_equal(mask.cpu().numpy().astype(bool), m_ref)
