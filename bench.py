@@ -216,6 +216,8 @@ def main() -> int:
     ap.add_argument("--per-config", default="all",
                     help="'all', 'none', or a comma list of c1..c5 timed cold after the main run")
     ap.add_argument("--reps", type=int, default=50, help="timed reps per workload in per_config")
+    ap.add_argument("--no-two-stream", action="store_true",
+                    help="skip the two-batch, two-stream context figure (profiled runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"after timing, copy {COPY_BYTES} bytes three times (counter scaling)")
     args = ap.parse_args()
@@ -252,16 +254,18 @@ def main() -> int:
     # Context only (not `value`): two independent batches alternating on two streams,
     # so that one batch's draws can overlap the other's streaming (as two micro-batches
     # of a server would); each plan has its own workspace.
-    side = torch.cuda.Stream(dev)
-    streams = [stream, side]
-    for i in range(args.warmup):
-        plans[i % len(plans)](streams[i % 2].cuda_stream)
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        plans[i % len(plans)](streams[i % 2].cuda_stream)
-    torch.cuda.synchronize(dev)
-    two_stream_ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    two_stream_ms = None
+    if not args.no_two_stream:
+        side = torch.cuda.Stream(dev)
+        streams = [stream, side]
+        for i in range(args.warmup):
+            plans[i % len(plans)](streams[i % 2].cuda_stream)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            plans[i % len(plans)](streams[i % 2].cuda_stream)
+        torch.cuda.synchronize(dev)
+        two_stream_ms = 1e3 * (time.perf_counter() - t0) / args.steps
 
     # Dominant kernel: the streaming normaliser over the same 1088 rows, timed with
     # HIP events on the launch stream (the normalise entry point launches it plus a
@@ -310,10 +314,10 @@ def main() -> int:
         "config": {"workload": "B=64, gamma=8, V=128256 bf16 Zipf logits, per-row T in "
                                "{0.1,0.4,0.7,1.0}, K=1", "B": w.B, "K": w.K, "gamma": w.gamma,
                    "V": w.V, "logits": "bf16", "input_copies_cycled": args.copies},
-        "two_batch_streams": {"ms_per_step": two_stream_ms,
-                              "tokens_per_s": tokens_per_step / (two_stream_ms * 1e-3),
-                              "note": "context only: two independent batches alternating on "
-                                      "two streams; value is one step at a time"},
+        "two_batch_streams": None if two_stream_ms is None else {
+            "ms_per_step": two_stream_ms, "tokens_per_s": tokens_per_step / (two_stream_ms * 1e-3),
+            "note": "context only: two independent batches alternating on two streams; value is "
+                    "one step at a time"},
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "bytes_min_per_step": bytes_min,
