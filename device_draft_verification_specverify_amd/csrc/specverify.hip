@@ -1,28 +1,35 @@
 // specverify.hip -- HIP kernels (gfx950 / CDNA4) and the C ABI of libspecverify.
 //
-// Batched speculative-sampling verification in three launches (a fourth only
-// past 65536 chains):
+// Batched speculative-sampling verification in two launches when the draw grid
+// is resident at once, otherwise three (accept_kernel derives n per chain
+// before the draws), and one more past 65536 chains:
 //
 //   stream_kernel   every needed logit row is read exactly once. Persistent
-//                   wavefronts walk 8 KB chunks of the flattened rows round
-//                   robin; draft rows of greedy batch rows are left out. Each
-//                   lane reduces its logits to (max, sum of exp2) with one fma +
-//                   one exp per logit; each chunk ends in one cross-lane
+//                   workgroups (one per CU) walk 8 KB chunks of the flattened
+//                   rows round robin, their wavefronts claiming chunks from an
+//                   LDS counter; draft rows of greedy batch rows are left out.
+//                   Each lane reduces its logits to (max, sum of exp2) with one
+//                   fma + one exp per logit; each chunk ends in one cross-lane
 //                   reduction and one 16-byte partial.
-//   accept_kernel   one workgroup per chain. It merges the partials of the
-//                   chain's rows into ln Z (each row once), gathers ln p / ln q
-//                   at the draft tokens, draws the accept uniforms and finds the
-//                   first rejection n with one wavefront ballot.
-//   draw_kernel     one workgroup per (chain, vocabulary split). It scans its
-//                   split of the one row pair the chain needs -- target/draft
-//                   row n for the residual, target row gamma for the bonus --
-//                   drawing Gumbel noise by exponential race, argmin_v E_v / w_v
-//                   with E_v = -ln u_v (the same argmax as ln w_v + G_v), keeps
-//                   its best two candidates and re-scores them in float64. The
-//                   last split of a chain to finish (a per-chain counter) keeps
-//                   the best score over the splits (ties to the lowest id).
+//   draw_kernel     one workgroup per (chain, vocabulary split). Each first
+//                   derives its chain's n (or reads it from accept_kernel,
+//                   which does the same per chain): ln Z of the chain's rows from the
+//                   partials (8 lanes per row), ln p / ln q at the draft tokens,
+//                   the accept uniforms and the first rejection by one ballot
+//                   (split 0 writes the chain's outputs). Then it scans its split
+//                   of the one row pair the chain needs -- target/draft row n for
+//                   the residual, target row gamma for the bonus -- drawing
+//                   Gumbel noise by exponential race, argmin_v E_v / w_v with
+//                   E_v = -ln u_v (the same argmax as ln w_v + G_v), keeps its
+//                   best two candidates and re-scores them in float64. The last
+//                   split of a chain to finish (a per-chain counter) keeps the
+//                   best score over the splits (ties to the lowest id).
 //   finish_kernel   that last step, one wavefront per chain, when there are too
 //                   many chains for the counters.
+//
+// The other entry points (normalise, accept test, residual sample, acceptance
+// probability, top-F candidates, cache lookup, branch pruning) reuse these
+// pieces; each kernel below says which.
 //
 // Hand-offs inside a launch (the per-chain counters) use relaxed agent-scope
 // atomics after the publishing wavefront's stores have completed.
@@ -91,7 +98,8 @@ struct alignas(16) Cand {
   int32_t pad;
 };
 
-// What the draw and finish kernels need of a chain (written by the accept kernel).
+// What the draw and finish kernels need of a chain (written by split 0 of the
+// step's draw kernel, or by given_kernel).
 struct alignas(16) ChainInfo {
   double lzt;  // ln Z of the target row the token is drawn from (row n, or gamma)
   double lzd;  // ln Z of draft row n (residual draws)
@@ -795,7 +803,7 @@ struct ChainArgs {
   const int32_t* tokens;     // [B, K, G]
   uint64_t seed;
   const int64_t* pos0;
-  // outputs (accept kernel; out_token of a sampled chain: draw kernel)
+  // outputs (split 0 of the draw kernel's chain; out_token of a sampled chain: its last split)
   int32_t* accept_len;
   int32_t* out_token;
   float* logp;
@@ -808,25 +816,26 @@ struct ChainArgs {
   const double* lnz_d_in;    // [B, K, G]
   const int32_t* amax_in;    // [B, G+1]
   const int32_t* n_in;       // [B, K]
-  // accept kernel -> draw kernel (-> finish kernel)
+  // draw kernel (split 0) or given_kernel -> (finish kernel)
   int64_t nsplit;
   Cand* cand;                // [B*K][nsplit]
   ChainInfo* info;           // [B*K]
   uint32_t* cnt;             // [B*K] splits done per chain, or null: finish_kernel picks the token
 };
 
-// One workgroup per chain: the normalisers of the chain's rows from the stream
-// partials, ln p / ln q at the draft tokens, the accept uniforms and the first
-// rejection by one wavefront ballot. It writes the chain's outputs and, for the
-// draw kernel, ChainInfo: n and the normalisers the draw needs. GIVEN
-// (specverify_residual_sample): n and the normalisers are inputs. Every row is
-// merged once per chain here, not once per vocabulary split.
+// The step's accept stage as its own launch, for grids too large to be
+// resident at once (then every split repeating the prologue would cost a
+// round of latency per dispatch round): one workgroup per chain merges the
+// chain's rows from the stream partials, gathers ln p / ln q at the draft
+// tokens, draws the accept uniforms and finds the first rejection by one
+// wavefront ballot. It writes the chain's outputs and the draw kernel's
+// ChainInfo.
 constexpr int kAcceptBlock = 1024;
 constexpr int kAcceptWaves = kAcceptBlock / kWave;
 constexpr int kAcceptRows = 2;  // rows per wavefront per pass
 static_assert(kAcceptWaves * kAcceptRows >= 17, "one pass covers a gamma = 8 chain");
 
-template <int DT, bool GIVEN>
+template <int DT>
 __global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   __shared__ double s_lnz[kMaxRowsPerChain];
@@ -845,19 +854,7 @@ __global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
   const bool sampled = T > 0.0f;
   const bool greedy = T == 0.0f;
 
-  if (GIVEN) {
-    if (t == 0) {
-      const int32_t n = a.n_in[chain];
-      s_n = (n < 0 || n > G) ? -1 : n;
-    }
-    if (t < P) {
-      s_lnz[t] = a.lnz_t_in[b * P + t];
-      s_amax[t] = a.amax_in[b * P + t];
-    }
-    if (t < G) s_lnz[P + t] = a.lnz_d_in[chain * G + t];
-    __syncthreads();
-    if (greedy && t == 0 && s_n >= 0) a.out_token[chain] = s_amax[s_n];
-  } else {
+  {
     // The merges of the chain's rows (target rows 0..G, then draft rows
     // (k, 0..G-1) when sampled) go first: wavefront w merges rows w, w + W
     // (W wavefronts), the partial loads of both rows in flight together. The
@@ -976,24 +973,207 @@ __global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
   }
 }
 
-// One workgroup per (chain, split of kSplit ids) of every chain that draws.
-// At least 4 waves per SIMD: 16 workgroups' worth of waves per CU, so the
-// usual grids run in one round.
-template <int DT, bool VEC>
+// specverify_residual_sample: one thread per chain turns the given n and
+// normalisers into the draw kernel's ChainInfo (greedy rows: the token is the
+// target row's argmax at n).
+__global__ __launch_bounds__(kBlock) void given_kernel(ChainArgs a, int64_t chains) {
+  const int64_t chain = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+  if (chain >= chains) return;
+  const RowSet& rs = a.rs;
+  const int64_t b = chain / rs.K;
+  const int G = int(rs.G);
+  const int P = G + 1;
+  const float T = rs.temp[b];
+  const bool sampled = T > 0.0f;
+  const int32_t n0 = a.n_in[chain];
+  const int n = (n0 < 0 || n0 > G) ? -1 : n0;
+  if (T == 0.0f && n >= 0) a.out_token[chain] = a.amax_in[b * P + n];
+  ChainInfo ci;
+  ci.n = (n >= 0 && sampled) ? n : -1;
+  ci.lzt = n >= 0 ? a.lnz_t_in[b * P + n] : 0.0;
+  ci.lzd = (n >= 0 && n < G && sampled) ? a.lnz_d_in[chain * G + n] : 0.0;
+  ci.pad[0] = ci.pad[1] = ci.pad[2] = 0;
+  a.info[chain] = ci;
+}
+
+// Per-chain prologue of the step's draw kernel: every split of a chain derives
+// the chain's n itself, so no separate accept launch sits between the stream
+// and the draws. The rows' ln Z come from the stream partials with 8 lanes per
+// row (up to 32 rows per pass of the workgroup, a 3-step reduction per row);
+// the draft-token logits load while the partials fold. Split 0 writes the
+// chain's outputs. Returns n in LDS (-1: nothing to draw or an error).
+constexpr int kRowLanes = 8;
+constexpr int kRowsPerPass = kBlock / kRowLanes;
+
+template <int DT>
+__device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, double* s_lnz,
+                               int32_t* s_amax, int32_t* s_rowbad, int32_t* s_n) {
+  constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  const RowSet& rs = a.rs;
+  const int64_t b = chain / rs.K;
+  const int64_t k = chain - b * rs.K;
+  const int G = int(rs.G);
+  const int P = G + 1;
+  const int t = threadIdx.x;
+  const float T = rs.temp[b];
+  const bool sampled = T > 0.0f;
+  const bool greedy = T == 0.0f;
+  const double k2 = double(kLog2e / T);
+  int32_t x = 0;
+  bool tok_bad = false;
+  if (t < G) {
+    x = a.tokens[chain * G + t];
+    tok_bad = x < 0 || int64_t(x) >= a.V;
+  }
+  const int grp = t / kRowLanes;
+  const int gl = t % kRowLanes;
+  const int nr = P + (sampled ? G : 0);
+  int32_t bad = 0;
+  float zt = 0.0f, zd = 0.0f;
+  double log_u = 0.0;
+  for (int base = 0; base < nr; base += kRowsPerPass) {
+    const int ri = base + grp;
+    const bool has = ri < nr;
+    const int64_t rho = !has ? 0 : ri < P ? b * P + ri : rs.B * P + chain * G + (ri - P);
+    float m = -INFINITY;
+    int32_t idx = INT_MAX;
+    double s = 0.0;
+    for (int64_t c0 = gl; c0 < a.cpr; c0 += 4 * kRowLanes) {
+      RowPartial q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + int64_t(u) * kRowLanes;
+        q[u] = (has && c < a.cpr) ? a.part[rho * a.cpr + c] : RowPartial{-INFINITY, INT_MAX, 0.0};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fold_partial(m, idx, s, q[u], sampled, k2);
+    }
+    if (base == 0 && t < G) {
+      // the logits at the draft tokens and the accept uniforms, while the rows reduce
+      if (!tok_bad && sampled) {
+        zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + t * rs.tsj), x);
+        zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + t * rs.dsj), x);
+      }
+      const uint64_t pos = uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(t);
+      const Philox4 r = philox4x32_10(0u, uint32_t(pos), uint32_t(chain), kPurposeAccept,
+                                      uint32_t(a.seed), uint32_t(a.seed >> 32));
+      log_u = log_uniform_d(unit_uniform_d(r.w[0]));
+    }
+    // combine the 8 lanes of each row in a fixed order
+    float M = m;
+    int32_t I = idx;
+#pragma unroll
+    for (int off = kRowLanes / 2; off > 0; off >>= 1) {
+      const float om = __shfl_xor(M, off, kWave);
+      const int32_t oi = __shfl_xor(I, off, kWave);
+      better_max(M, I, om, oi);
+    }
+    double sr = 0.0;
+    if (sampled && M > -INFINITY) sr = m > -INFINITY ? s * exp2_scale((double(m) - double(M)) * k2) : 0.0;
+#pragma unroll
+    for (int off = kRowLanes / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
+    if (has && gl == 0) {
+      double lnz;
+      if (sampled) lnz = M > -INFINITY ? double(M) / double(T) + log(sr) : double(M);
+      else if (greedy) lnz = double(M);
+      else lnz = NAN;
+      s_lnz[ri] = lnz;
+      if (!(M > -INFINITY)) bad = SV_ERR_ROW;
+      if (ri < P) {
+        s_amax[ri] = I == INT_MAX ? 0 : I;
+        if (lead && k == 0 && a.lnz_t_out) a.lnz_t_out[b * P + ri] = lnz;
+      } else if (lead && a.lnz_d_out) {
+        a.lnz_d_out[chain * G + (ri - P)] = lnz;
+      }
+    }
+  }
+  if (gl == 0) s_rowbad[grp] = bad;
+  __syncthreads();
+  // accept tests of the G positions in wavefront 0, first rejection by ballot
+  if (t < kWave) {
+    bool acc = false;
+    if (t < G) {
+      const int j = t;
+      double lp = 0.0, lq = 0.0;
+      if (!tok_bad) {
+        if (sampled) {
+          lp = double(zt) / double(T) - s_lnz[j];
+          lq = double(zd) / double(T) - s_lnz[P + j];
+          acc = log_u < lp - lq;
+        } else if (greedy) {
+          acc = x == s_amax[j];
+          lp = acc ? 0.0 : -INFINITY;
+          lq = 0.0;
+        }
+      }
+      if (lead && a.logp) a.logp[chain * G + j] = float(lp);
+      if (lead && a.logq) a.logq[chain * G + j] = float(lq);
+    }
+    const uint64_t acc_mask = __ballot(acc);
+    const uint64_t bad_mask = __ballot(tok_bad);
+    if (t == 0) {
+      const int n = __builtin_ctzll(~acc_mask);  // leading accepts (<= G: bit G of ~mask is set)
+      int32_t err = 0;
+      for (int g = 0; g < kRowsPerPass; ++g) err |= s_rowbad[g];
+      if (bad_mask) err |= SV_ERR_TOKEN;
+      if (!(sampled || greedy)) err |= SV_ERR_TEMP;
+      *s_n = (err || !sampled) ? -1 : n;
+      if (lead) {
+        if (err) {
+          a.accept_len[chain] = -1;
+          a.out_token[chain] = -1;
+          if (a.dev_err) atomicOr(a.dev_err, err);
+        } else {
+          a.accept_len[chain] = n;
+          if (greedy) a.out_token[chain] = s_amax[n];
+        }
+        ChainInfo ci;
+        ci.n = (!err && sampled) ? n : -1;
+        ci.lzt = !err ? s_lnz[n] : 0.0;
+        ci.lzd = (!err && sampled && n < G) ? s_lnz[P + n] : 0.0;
+        ci.pad[0] = ci.pad[1] = ci.pad[2] = 0;
+        a.info[chain] = ci;  // for finish_kernel past the counted chains
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// One workgroup per (chain, split of kSplit ids). FUSED (the step): the
+// workgroup derives n and the normalisers itself (chain_prologue); otherwise
+// (specverify_residual_sample) it reads them from given_kernel's ChainInfo. At least 4 waves per SIMD: 16 workgroups' worth of waves per CU,
+// so the usual grids run in one round.
+template <int DT, bool VEC, bool FUSED>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void draw_kernel(ChainArgs a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   __shared__ Top2 s_top[kWavesPerBlock];
   __shared__ uint32_t s_last;
+  __shared__ double s_lnz[kMaxRowsPerChain];
+  __shared__ int32_t s_amax[SV_MAX_GAMMA + 1];
+  __shared__ int32_t s_rowbad[kRowsPerPass];
+  __shared__ int32_t s_n;
   const RowSet& rs = a.rs;
   const int64_t chain = blockIdx.x / a.nsplit;
   const int64_t split = blockIdx.x - chain * a.nsplit;
-  const ChainInfo ci = a.info[chain];
-  const int n = ci.n;
-  if (n < 0) return;  // uniform across the workgroup: this chain draws nothing
+  const int G = int(rs.G);
+  int n;
+  double lzt_c, lzd_c;
+  if (FUSED) {
+    chain_prologue<DT>(a, chain, split == 0, s_lnz, s_amax, s_rowbad, &s_n);
+    n = s_n;
+    if (n < 0) return;  // uniform across the workgroup: this chain draws nothing
+    lzt_c = s_lnz[n];
+    lzd_c = n < G ? s_lnz[G + 1 + n] : 0.0;
+  } else {
+    const ChainInfo ci = a.info[chain];
+    n = ci.n;
+    if (n < 0) return;
+    lzt_c = ci.lzt;
+    lzd_c = ci.lzd;
+  }
   const int64_t b = chain / rs.K;
   const int64_t k = chain - b * rs.K;
-  const int G = int(rs.G);
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const float T = rs.temp[b];
@@ -1003,8 +1183,8 @@ void draw_kernel(ChainArgs a) {
   const void* row_t = row_ptr(rs.t, esz, b * rs.tsb + int64_t(n) * rs.tsj);
   const void* row_d =
       residual ? row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + int64_t(n) * rs.dsj) : row_t;
-  const double lzt = ci.lzt;
-  const double lzd = residual ? ci.lzd : 0.0;
+  const double lzt = lzt_c;
+  const double lzd = residual ? lzd_c : 0.0;
   DrawParams dp;
   dp.k2 = kLog2e / T;
   dp.L2t = float(lzt * kLog2eD);
@@ -1728,14 +1908,47 @@ void launch_stream(int dtype, bool vec, bool argmax_all, const StreamArgs& sa, h
                   : launch_stream_t<SV_F32, false, false>(sa, st);
 }
 
+// Workgroups of the fused draw kernel resident on the device at once (cached per
+// device).
+template <int DT, bool VEC>
+int64_t draw_resident() {
+  static std::atomic<int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, draw_kernel<DT, VEC, true>, kBlock,
+                                                   0) != hipSuccess ||
+      blocks <= 0)
+    blocks = 4;
+  const int64_t n = int64_t(cus) * blocks;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int DT, bool VEC>
 void launch_chain_finish(const ChainArgs& ca, bool given, hipStream_t st) {
   const int64_t chains = ca.rs.B * ca.rs.K;
-  const dim3 one{unsigned(chains), 1u, 1u};
-  if (given) hipLaunchKernelGGL((accept_kernel<DT, true>), one, dim3(kAcceptBlock), 0, st, ca);
-  else hipLaunchKernelGGL((accept_kernel<DT, false>), one, dim3(kAcceptBlock), 0, st, ca);
   const dim3 grid{unsigned(chains * ca.nsplit), 1u, 1u};
-  hipLaunchKernelGGL((draw_kernel<DT, VEC>), grid, dim3(kBlock), 0, st, ca);
+  if (given) {
+    hipLaunchKernelGGL(given_kernel, dim3(unsigned((chains + kBlock - 1) / kBlock)), dim3(kBlock),
+                       0, st, ca, chains);
+    hipLaunchKernelGGL((draw_kernel<DT, VEC, false>), grid, dim3(kBlock), 0, st, ca);
+  } else if (chains * ca.nsplit <= draw_resident<DT, VEC>()) {
+    // every split derives n itself: one launch fewer, one prologue per workgroup
+    hipLaunchKernelGGL((draw_kernel<DT, VEC, true>), grid, dim3(kBlock), 0, st, ca);
+  } else {
+    // more workgroups than fit at once: n per chain in its own launch
+    hipLaunchKernelGGL((accept_kernel<DT>), dim3(unsigned(chains)), dim3(kAcceptBlock), 0, st, ca);
+    hipLaunchKernelGGL((draw_kernel<DT, VEC, false>), grid, dim3(kBlock), 0, st, ca);
+  }
   if (ca.cnt) return;  // the chains' last splits picked the tokens
   const RowSet& rs = ca.rs;
   hipLaunchKernelGGL((finish_kernel<DT, VEC>), dim3(unsigned(chains)), dim3(kWave), 0, st, rs.t,
