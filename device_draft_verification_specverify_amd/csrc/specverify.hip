@@ -747,12 +747,36 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
 // lane share one address and differ by immediate offsets; all of them are
 // issued before any is scored, and the scoring loop is not unrolled (it walks
 // a window of registers that shifts by one vector per pass).
+//
+// When no vector of the split is partial (every split when V is a multiple of
+// 8, else all but the row's last), the loads are issued unconditionally (lanes
+// past the row load the row's last vector and never score it) and the scoring
+// is unrolled, so vector it waits only for its own loads and the arithmetic of
+// the first vectors overlaps the arrival of the later ones.
 template <int DT, bool VEC, bool RESIDUAL>
 __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d, int64_t split,
                                            int64_t V, const DrawParams& dp) {
   const int64_t vpr = (V + kVec - 1) / kVec;
   const int64_t vi0 = split * (kSplit / kVec) +
                       int64_t(threadIdx.x / kWave) * (kWave * kSampleIters) + (threadIdx.x & (kWave - 1));
+  const bool whole = VEC && (V % kVec == 0 || (split + 1) * (kSplit / kVec) < vpr);
+  if (whole) {
+    RawVec<DT> wt[kSampleIters], wd[kSampleIters];
+#pragma unroll
+    for (int it = 0; it < kSampleIters; ++it) {
+      const int64_t vi = vi0 + int64_t(kWave) * it;
+      const int64_t vc = vi < vpr ? vi : vpr - 1;
+      wt[it] = load_vec<DT, true>(row_t, vc);
+      if constexpr (RESIDUAL) wd[it] = load_vec<DT, true>(row_d, vc);
+    }
+    Top2 best = top2_empty();
+#pragma unroll
+    for (int it = 0; it < kSampleIters; ++it) {
+      const int64_t vi = vi0 + int64_t(kWave) * it;
+      if (vi < vpr) score_vec<DT, RESIDUAL>(wt[it], RESIDUAL ? wd[it] : wt[it], vi, dp, best);
+    }
+    return best;
+  }
   RawVec<DT> rt[kSampleIters], rd[kSampleIters];
 #pragma unroll
   for (int it = 0; it < kSampleIters; ++it) {
