@@ -208,8 +208,9 @@ def per_config(names, reps: int, warmup: int, dev) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first; the clocks settle within a few hundred steps")
     ap.add_argument("--copies", type=int, default=4,
                     help="input copies cycled so consecutive steps never reuse cached logits")
     ap.add_argument("--no-cpu", action="store_true")
