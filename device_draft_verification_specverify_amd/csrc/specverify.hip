@@ -401,6 +401,24 @@ __device__ int64_t select_sampled(const SampledTable& tab, int nchunks, int64_t 
   return int64_t(lo) * 64 + __builtin_ctzll(m);
 }
 
+// Division of n < 2^31 by an invariant divisor d >= 1 as a multiply-high and a
+// shift (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, figure 4.1): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l. mulhi(m, n)
+// is at most n, so the sum stays below 2^32 for n < 2^31.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+  return FastDiv{d, uint32_t(m), l};
+}
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.m) + n) >> f.l;
+}
+
 struct StreamArgs {
   RowSet rs;
   int64_t V, vpr;
@@ -409,6 +427,9 @@ struct StreamArgs {
   int compact;
   RowPartial* part;      // [B*(P+K*G)][cpr]: slot b*P+j, then B*P + (b*K+k)*G+j
   int32_t* rank_out;     // [B + 1]: sampled batch rows before b; [B] = their total
+  // The chunk-index divisions (by cpr, P, K*G, G) as multiply-shifts: every
+  // chunk index is below 2^31 (the host rejects larger calls).
+  FastDiv by_cpr, by_p, by_kg, by_g;
 };
 
 // Persistent workgroups (one per CU) walk the chunks of the flattened stream
@@ -452,7 +473,7 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
   while (c < total) {
     uint32_t next = 0;
     if (lane == 0) next = atomicAdd(&s_claim, 1u);  // the next claim, answered during the loads
-    const int64_t rho = c / a.cpr;
+    const int64_t rho = fast_div(uint32_t(c), a.by_cpr);
     const int64_t v0 = (c - rho * a.cpr) * cv;
     const int64_t v1 = v0 + cv < a.vpr ? v0 + cv : a.vpr;
     const void* row;
@@ -460,16 +481,16 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
     int64_t slot = rho;  // partials sit by batch row: target rows, then draft rows (b, k, j)
     bool is_draft;
     if (rho < BP) {
-      b = rho / rs.P;
+      b = fast_div(uint32_t(rho), a.by_p);
       const int64_t j = rho - b * rs.P;
       row = row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj);
       is_draft = false;
     } else {
       const int64_t d = rho - BP;
-      const int64_t sidx = d / KG;
+      const int64_t sidx = fast_div(uint32_t(d), a.by_kg);
       b = a.compact ? select_sampled(tab, nchunks, sidx) : sidx;
       const int64_t rem = d - sidx * KG;
-      const int64_t k = rem / rs.G;
+      const int64_t k = fast_div(uint32_t(rem), a.by_g);
       const int64_t j = rem - k * rs.G;
       row = row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj);
       is_draft = true;
@@ -1364,6 +1385,7 @@ struct OverlapArgs {
   const double* lnz_t;     // [B, G+1]
   const double* lnz_d;     // [B, K, G]
   OverlapPartial* part;    // [(b*K + k)*G + j][cpr]
+  FastDiv by_cpr, by_g;    // unit indices are below 2^31 (checked on the host)
 };
 
 // One sweep over the target rows 0..G-1 and every draft row. A unit is
@@ -1396,9 +1418,9 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
   while (c < total) {
     uint32_t next = 0;
     if (lane == 0) next = atomicAdd(&s_claim, 1u);
-    const int64_t bj = c / a.cpr;
+    const int64_t bj = fast_div(uint32_t(c), a.by_cpr);
     const int64_t chunk = c - bj * a.cpr;
-    const int64_t b = bj / G;
+    const int64_t b = fast_div(uint32_t(bj), a.by_g);
     const int64_t j = bj - b * G;
     const int64_t v0 = chunk * cv;
     const int64_t v1 = v0 + cv < a.vpr ? v0 + cv : a.vpr;
@@ -1918,7 +1940,14 @@ void launch_stream_t(const StreamArgs& sa, hipStream_t st) {
                      dim3(kStreamBlock), 0, st, sa);
 }
 
-void launch_stream(int dtype, bool vec, bool argmax_all, const StreamArgs& sa, hipStream_t st) {
+void launch_stream(int dtype, bool vec, bool argmax_all, StreamArgs sa, hipStream_t st) {
+  // chunk indices are below 2^31 (stream_chunks_ok): the kernel divides by
+  // multiply-shift
+  const int64_t kg = sa.rs.K * sa.rs.G;
+  sa.by_cpr = make_fastdiv(uint32_t(sa.cpr));
+  sa.by_p = make_fastdiv(uint32_t(sa.rs.P));
+  sa.by_kg = make_fastdiv(uint32_t(kg > 0 ? kg : 1));
+  sa.by_g = make_fastdiv(uint32_t(sa.rs.G > 0 ? sa.rs.G : 1));
   if (dtype == SV_BF16) {
     if (vec) argmax_all ? launch_stream_t<SV_BF16, true, true>(sa, st)
                         : launch_stream_t<SV_BF16, true, false>(sa, st);
@@ -2009,6 +2038,10 @@ bool workspace_ok(void* ws, size_t have, size_t need, int* status) {
   }
   return true;
 }
+
+// The stream kernel indexes chunks in 32 bits: fewer than 2^31 chunks per call
+// (2^31 chunks of 8 KB are 16 TiB of logits).
+bool stream_chunks_ok(const Layout& L) { return L.nrows * L.cpr < (int64_t(1) << 31); }
 
 Layout step_layout(int64_t B, int64_t K, int64_t G, int64_t V, int dtype) {
   return make_layout(B, B * (G + 1) + B * K * G, B * K, V, dtype);
@@ -2103,6 +2136,7 @@ int specverify_normalize(const void* logits, int dtype, int64_t B, int64_t P, in
     return SV_EINVAL;
   if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
   const Layout L = make_layout(B, B * P, 0, V, dtype);
+  if (!stream_chunks_ok(L)) return SV_EINVAL;
   int status = SV_OK;
   if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
   const int esz = esize(dtype);
@@ -2197,6 +2231,7 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
     return SV_EINVAL;
   if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
   const Layout L = step_layout(B, K, gamma, V, dtype);
+  if (!stream_chunks_ok(L)) return SV_EINVAL;
   int status = SV_OK;
   if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
   const int esz = esize(dtype);
@@ -2293,6 +2328,9 @@ int specverify_accept_prob(const void* target_logits, const void* draft_logits, 
   oa.lnz_d = lnZ_draft;
   oa.part = reinterpret_cast<OverlapPartial*>(reinterpret_cast<char*>(workspace) + kCounterBytes);
   const int64_t units = B * gamma * oa.cpr;
+  if (units >= (int64_t(1) << 31)) return SV_EINVAL;  // 32-bit unit indices
+  oa.by_cpr = make_fastdiv(uint32_t(oa.cpr));
+  oa.by_g = make_fastdiv(uint32_t(gamma));
   if (dtype == SV_BF16) {
     if (vec) launch_overlap<SV_BF16, true>(oa, units, st);
     else launch_overlap<SV_BF16, false>(oa, units, st);

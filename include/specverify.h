@@ -107,7 +107,8 @@ size_t specverify_workspace_size(int64_t B, int64_t K, int64_t gamma, int64_t V,
  *   argmax       [B, P] int32 out, or NULL: lowest id of the row maximum of
  *                the raw logits, for every row.
  * Status: SV_EINVAL (null logits/temperature/lnZ, B/P/V < 1, V >= 2^31,
- * negative stride), SV_EDTYPE, SV_EWORKSPACE, SV_EALIGN, SV_EHIP.
+ * negative stride, or rows of 2^31 or more 8 KB chunks: over 16 TiB of
+ * logits), SV_EDTYPE, SV_EWORKSPACE, SV_EALIGN, SV_EHIP.
  */
 int specverify_normalize(const void* logits, int dtype, int64_t B, int64_t P, int64_t V,
                          int64_t stride_b, int64_t stride_p, const float* temperature,
@@ -182,8 +183,9 @@ int specverify_residual_sample(const void* target_logits, const void* draft_logi
  *   device_error   one int32 out or NULL: OR of SV_ERR_* bits (only set, never
  *                  cleared: zero it before the call)
  * Status: SV_EINVAL (null required pointer, B/K/V < 1, gamma outside [1, 32],
- * K*gamma > 64, V >= 2^31, negative stride), SV_EDTYPE, SV_EWORKSPACE,
- * SV_EALIGN, SV_EHIP.
+ * K*gamma > 64, V >= 2^31, negative stride, or rows of 2^31 or more 8 KB
+ * chunks: over 16 TiB of logits), SV_EDTYPE, SV_EWORKSPACE, SV_EALIGN,
+ * SV_EHIP.
  */
 int specverify_step(const void* target_logits, const void* draft_logits, int dtype,
                     const int32_t* draft_tokens, int64_t B, int64_t K, int64_t gamma, int64_t V,

@@ -93,6 +93,9 @@ def test_other_entry_points_validate_on_the_host():
     assert lib.specverify_normalize(None, 1, 2, 3, 100, 300, 100, 8, 8, None, 256, 1 << 20, None) == -1
     assert lib.specverify_normalize(8, 9, 2, 3, 100, 300, 100, 8, 8, None, 256, 1 << 20, None) == -2
     assert lib.specverify_normalize(8, 1, 2, 3, 100, 300, 100, 8, 8, None, 256, 16, None) == -3
+    # 2^31 or more 8 KB chunks in one call (over 16 TiB of rows): rejected before any HIP call
+    assert lib.specverify_normalize(8, 1, 2 ** 27, 1, 2 ** 20, 0, 0, 8, 8, None, 256, 1 << 20,
+                                    None) == -1
     assert lib.specverify_accept(None, 8, 2, 1, 4, 0, None, 8, None, None) == -1
     assert lib.specverify_accept(8, 8, 2, 1, 33, 0, None, 8, None, None) == -1
     assert lib.specverify_accept(8, 8, 0, 1, 4, 0, None, 8, None, None) == -1
