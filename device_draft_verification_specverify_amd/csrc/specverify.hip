@@ -396,9 +396,21 @@ __device__ int64_t select_sampled(const SampledTable& tab, int nchunks, int64_t 
     if (tab.pref[mid] <= s) lo = mid;
     else hi = mid - 1;
   }
+  // the r-th (from 0) set bit of the chunk's mask, by halving: keep the low
+  // half while it holds more than r set bits, else skip it
   uint64_t m = tab.mask[lo];
-  for (int64_t r = s - tab.pref[lo]; r > 0; --r) m &= m - 1;
-  return int64_t(lo) * 64 + __builtin_ctzll(m);
+  int r = int(s - tab.pref[lo]);
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) {
+    const int c = __popcll(m & ((uint64_t(1) << w) - 1));
+    if (r >= c) {
+      r -= c;
+      m >>= w;
+      pos += w;
+    }
+  }
+  return int64_t(lo) * 64 + pos;
 }
 
 // Division of n < 2^31 by an invariant divisor d >= 1 as a multiply-high and a
