@@ -878,6 +878,9 @@ struct ChainArgs {
   Cand* cand;                // [B*K][nsplit]
   ChainInfo* info;           // [B*K]
   uint32_t* cnt;             // [B*K] splits done per chain, or null: finish_kernel picks the token
+  // workgroup -> (chain, split) and chain -> (b, k) as multiply-shifts (B*K*nsplit < 2^31);
+  // the fused draw kernel divides in 32 bits instead (measured faster there)
+  FastDiv by_nsplit, by_k;
 };
 
 // The step's accept stage as its own launch, for grids too large to be
@@ -901,7 +904,7 @@ __global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
   __shared__ int32_t s_n;
   const RowSet& rs = a.rs;
   const int64_t chain = blockIdx.x;
-  const int64_t b = chain / rs.K;
+  const int64_t b = fast_div(uint32_t(chain), a.by_k);
   const int64_t k = chain - b * rs.K;
   const int G = int(rs.G);
   const int P = G + 1;
@@ -1037,7 +1040,7 @@ __global__ __launch_bounds__(kBlock) void given_kernel(ChainArgs a, int64_t chai
   const int64_t chain = int64_t(blockIdx.x) * kBlock + threadIdx.x;
   if (chain >= chains) return;
   const RowSet& rs = a.rs;
-  const int64_t b = chain / rs.K;
+  const int64_t b = fast_div(uint32_t(chain), a.by_k);
   const int G = int(rs.G);
   const int P = G + 1;
   const float T = rs.temp[b];
@@ -1067,7 +1070,7 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
                                int32_t* s_amax, int32_t* s_rowbad, int32_t* s_n) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   const RowSet& rs = a.rs;
-  const int64_t b = chain / rs.K;
+  const int64_t b = int64_t(uint32_t(chain) / uint32_t(rs.K));
   const int64_t k = chain - b * rs.K;
   const int G = int(rs.G);
   const int P = G + 1;
@@ -1211,7 +1214,8 @@ void draw_kernel(ChainArgs a) {
   __shared__ int32_t s_rowbad[kRowsPerPass];
   __shared__ int32_t s_n;
   const RowSet& rs = a.rs;
-  const int64_t chain = blockIdx.x / a.nsplit;
+  const int64_t chain = FUSED ? int64_t(uint32_t(blockIdx.x) / uint32_t(a.nsplit))
+                              : int64_t(fast_div(blockIdx.x, a.by_nsplit));
   const int64_t split = blockIdx.x - chain * a.nsplit;
   const int G = int(rs.G);
   int n;
@@ -1229,7 +1233,7 @@ void draw_kernel(ChainArgs a) {
     lzt_c = ci.lzt;
     lzd_c = ci.lzd;
   }
-  const int64_t b = chain / rs.K;
+  const int64_t b = FUSED ? int64_t(uint32_t(chain) / uint32_t(rs.K)) : int64_t(fast_div(uint32_t(chain), a.by_k));
   const int64_t k = chain - b * rs.K;
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
@@ -2021,7 +2025,9 @@ void launch_chain_finish(const ChainArgs& ca, bool given, hipStream_t st) {
                      ca.cand, ca.nsplit, ca.out_token);
 }
 
-void launch_chain(int dtype, bool vec, const ChainArgs& ca, bool given, hipStream_t st) {
+void launch_chain(int dtype, bool vec, ChainArgs ca, bool given, hipStream_t st) {
+  ca.by_nsplit = make_fastdiv(uint32_t(ca.nsplit));
+  ca.by_k = make_fastdiv(uint32_t(ca.rs.K));
   if (dtype == SV_BF16) {
     if (vec) launch_chain_finish<SV_BF16, true>(ca, given, st);
     else launch_chain_finish<SV_BF16, false>(ca, given, st);
