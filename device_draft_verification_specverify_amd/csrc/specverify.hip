@@ -1609,6 +1609,7 @@ __global__ __launch_bounds__(kBlock) void alpha_law_kernel(const OverlapPartial*
 constexpr int kTopFBlock = 256;
 constexpr int kTopFCap = 4096;                   // LDS candidate buffer (entries)
 constexpr int kTopFBatch = kTopFBlock * kVec;    // ids scored per pass of the workgroup
+constexpr int kTopFSample = 8;                   // passes sampled for the first threshold
 
 struct TopFArgs {
   RowSet rs;
@@ -1667,8 +1668,8 @@ __device__ __forceinline__ void lds_barrier() {
 // ids whose score reaches the current threshold go to an LDS buffer; past 256
 // entries the buffer is sorted, cut to the best F_j, and the threshold becomes
 // the F_j-th score. The first threshold is the F_j-th largest of the threads'
-// maxima over the first pass (F_j distinct ids reach it, so it is no higher
-// than the row's F_j-th score). The next pass's vectors load while the
+// maxima over a sample of passes spread over the row (F_j distinct ids reach
+// it, so it is no higher than the row's F_j-th score). The next pass's vectors load while the
 // current one is scored. Scores: residual or target weights in float32 (the
 // exponent split in two floats so that large z/T costs no precision), raw
 // logits for greedy rows; -inf = not a candidate.
@@ -1715,9 +1716,58 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
   const float c_lo = float(l2t - double(c_hi));
   const float d2 = residual ? float((a.lnz_t[b * (G + 1) + j] - a.lnz_d[chain * G + j]) * kLog2eD)
                             : 0.0f;
-  if (tid == 0) {
-    s_cnt = 0;
-    s_thr = -INFINITY;
+  if (tid == 0) s_cnt = 0;
+  // The weight (float32 score) of id vi*8+t; -inf: not a candidate.
+  auto score_at = [&](const RawVec<DT>& rt, const RawVec<DT>& rd, int t) {
+    const float zt = vec_elem<DT>(rt, t);
+    if (greedy) return zt;
+    const float a2 = fmaf(zt, k_hi, -c_hi) + fmaf(zt, k_lo, -c_lo);
+    float w = __builtin_amdgcn_exp2f(a2);
+    if (residual) w -= __builtin_amdgcn_exp2f(a2 + fmaf(vec_elem<DT>(rd, t) - zt, k_hi, d2));
+    return w > 0.0f ? w : -INFINITY;
+  };
+  // First threshold: the F-th largest of the threads' maxima over a sample of
+  // kTopFSample passes spread evenly over the row. The sampled ids are
+  // distinct, so at least F of them reach it and it is no higher than the
+  // row's F-th weight; being taken over the whole row, it admits far fewer
+  // ids than the first pass alone would (fewer sorts of the buffer).
+  {
+    const int64_t passes = (a.vpr + kTopFBlock - 1) / kTopFBlock;
+    const int64_t pstride = passes > kTopFSample ? passes / kTopFSample : 1;
+    RawVec<DT> st[kTopFSample], sd[kTopFSample];
+#pragma unroll
+    for (int i = 0; i < kTopFSample; ++i) {
+      const int64_t vi = int64_t(i) * pstride * kTopFBlock + tid;
+      st[i] = neg_inf_vec<DT>();
+      sd[i] = st[i];
+      if (vi < a.vpr) {
+        st[i] = load_vec_bounded<DT, VEC>(trow, vi, a.V);
+        if (residual) sd[i] = load_vec_bounded<DT, VEC>(drow, vi, a.V);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kTopFSample; ++i)
+#pragma unroll
+      for (int t = 0; t < kVec; ++t) mx = fmaxf(mx, score_at(st[i], sd[i], t));
+    s_max[tid] = mx;
+    __syncthreads();
+    for (int kk = 2; kk <= kTopFBlock; kk <<= 1) {
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        const int ixj = tid ^ jj;
+        float mine = s_max[tid], other = s_max[ixj];
+        lds_barrier();
+        if (ixj > tid) {
+          const bool first = (tid & kk) == 0;
+          if ((other > mine) == first) {
+            s_max[tid] = other;
+            s_max[ixj] = mine;
+          }
+        }
+        lds_barrier();
+      }
+    }
+    if (tid == 0) s_thr = s_max[F - 1];
   }
   RawVec<DT> nt = neg_inf_vec<DT>(), nd = neg_inf_vec<DT>();
   if (tid < a.vpr) {
@@ -1735,48 +1785,9 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
       if (residual) nd = load_vec_bounded<DT, VEC>(drow, vn, a.V);
     }
     float sc[kVec];
-    float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < kVec; ++t) {
-      const float zt = vec_elem<DT>(rt, t);
-      float score = -INFINITY;
-      if (vi < a.vpr) {
-        if (greedy) {
-          score = zt;
-        } else {
-          const float a2 = fmaf(zt, k_hi, -c_hi) + fmaf(zt, k_lo, -c_lo);
-          float w = __builtin_amdgcn_exp2f(a2);
-          if (residual) w -= __builtin_amdgcn_exp2f(a2 + fmaf(vec_elem<DT>(rd, t) - zt, k_hi, d2));
-          score = w > 0.0f ? w : -INFINITY;
-        }
-      }
-      sc[t] = score;
-      mx = fmaxf(mx, score);
-    }
-    float thr;
-    if (base == 0) {
-      // first threshold: the F-th largest of the threads' maxima (sorted, largest first)
-      s_max[tid] = mx;
-      lds_barrier();
-      for (int kk = 2; kk <= kTopFBlock; kk <<= 1) {
-        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-          const int ixj = tid ^ jj;
-          float mine = s_max[tid], other = s_max[ixj];
-          lds_barrier();
-          if (ixj > tid) {
-            const bool first = (tid & kk) == 0;
-            if ((other > mine) == first) {
-              s_max[tid] = other;
-              s_max[ixj] = mine;
-            }
-          }
-          lds_barrier();
-        }
-      }
-      thr = s_max[F - 1];
-    } else {
-      thr = s_thr;
-    }
+    for (int t = 0; t < kVec; ++t) sc[t] = vi < a.vpr ? score_at(rt, rd, t) : -INFINITY;
+    const float thr = s_thr;
     int mine = 0;
 #pragma unroll
     for (int t = 0; t < kVec; ++t) {
@@ -1794,7 +1805,6 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
           ++slot;
         }
     }
-    if (base == 0 && tid == 0) s_thr = thr;
     lds_barrier();
     const int cnt = s_cnt;
     if (cnt > kTopFCap - kTopFBatch || cnt > 256) {  // cut to the best F
