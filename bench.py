@@ -270,7 +270,7 @@ def main() -> int:
 
     # Dominant kernel: the streaming normaliser over the same 1088 rows, timed with
     # HIP events on the launch stream (the normalise entry point launches it plus a
-    # one-wavefront-per-row finalise).
+    # finalise of eight lanes per row).
     ws = sv.workspace(w.B, 0, 2 * w.gamma, w.V, sv.SV_BF16, dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]

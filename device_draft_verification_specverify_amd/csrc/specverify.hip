@@ -353,6 +353,58 @@ __device__ __forceinline__ RowStat wave_reduce_row(float m, int32_t idx, double 
   return out;
 }
 
+// Statistics of one stream row by a group of kRowLanes consecutive lanes, for
+// rows of few chunks: lane gl of the group folds chunks gl, gl + 8, ..., four
+// loads in flight at a time (has == false: the lane folds nothing), and
+// group_reduce_row combines the group in a fixed order (xor 4, 2, 1). The
+// draws' prologue folds and combines its rows in this same order, inline, so
+// that both give a row the same bits. Every lane of the wavefront calls
+// group_reduce_row; all lanes of a group get the result, with lnZ as for
+// wave_reduce_row.
+constexpr int kRowLanes = 8;
+
+__device__ __forceinline__ void group_fold(const RowPartial* __restrict__ part, int64_t rho,
+                                           bool has, int64_t cpr, int gl, bool sampled, double k2,
+                                           float& m, int32_t& idx, double& s) {
+  m = -INFINITY;
+  idx = INT_MAX;
+  s = 0.0;
+  for (int64_t c0 = gl; c0 < cpr; c0 += 4 * kRowLanes) {
+    RowPartial q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = c0 + int64_t(u) * kRowLanes;
+      q[u] = (has && c < cpr) ? part[rho * cpr + c] : RowPartial{-INFINITY, INT_MAX, 0.0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fold_partial(m, idx, s, q[u], sampled, k2);
+  }
+}
+
+__device__ __forceinline__ RowStat group_reduce_row(float m, int32_t idx, double s, float T) {
+  const bool sampled = T > 0.0f;
+  const double k2 = double(kLog2e / T);
+  float M = m;
+  int32_t I = idx;
+#pragma unroll
+  for (int off = kRowLanes / 2; off > 0; off >>= 1) {
+    const float om = __shfl_xor(M, off, kWave);
+    const int32_t oi = __shfl_xor(I, off, kWave);
+    better_max(M, I, om, oi);
+  }
+  double sr = 0.0;
+  if (sampled && M > -INFINITY) sr = m > -INFINITY ? s * exp2_scale((double(m) - double(M)) * k2) : 0.0;
+#pragma unroll
+  for (int off = kRowLanes / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
+  RowStat out;
+  out.m = M;
+  out.idx = I;
+  if (sampled) out.lnz = M > -INFINITY ? double(M) / double(T) + log(sr) : double(M);
+  else if (T == 0.0f) out.lnz = double(M);
+  else out.lnz = NAN;
+  return out;
+}
+
 // ---------------------------------------------------------------------------
 // Which batch rows need draft rows: a ballot mask per 64 batch rows and an
 // exclusive prefix of their counts, built in LDS by every stream workgroup.
@@ -586,22 +638,26 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
   }
 }
 
-// ln Z and argmax of every row (specverify_normalize): one wavefront per row.
-__global__ __launch_bounds__(kBlock) void finalize_rows_kernel(const RowPartial* __restrict__ part,
-                                                               int64_t nrows, int64_t cpr, int64_t P,
-                                                               const float* __restrict__ temp,
-                                                               double* __restrict__ lnz,
-                                                               int32_t* __restrict__ amax) {
-  const int64_t rho = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-  if (rho >= nrows) return;
-  const int64_t rows[1] = {rho};
-  const float T = temp[rho / P];
-  float m[1];
-  int32_t idx[1];
-  double s[1];
-  lane_fold<1>(part, rows, cpr, T, m, idx, s);
-  const RowStat st = wave_reduce_row(m[0], idx[0], s[0], T);
-  if ((threadIdx.x & (kWave - 1)) == 0) {
+// ln Z and argmax of every row (specverify_normalize): eight lanes per row, the
+// same fold and reduction order as the draws' prologue, so both give a row the
+// same bits. Rows number fewer than 2^31 (the stream's chunk limit).
+constexpr int kFinBlock = 256;
+
+__global__ __launch_bounds__(kFinBlock) void finalize_rows_kernel(const RowPartial* __restrict__ part,
+                                                                  int64_t nrows, int64_t cpr, int64_t P,
+                                                                  const float* __restrict__ temp,
+                                                                  double* __restrict__ lnz,
+                                                                  int32_t* __restrict__ amax) {
+  const int64_t rho = int64_t(blockIdx.x) * (kFinBlock / kRowLanes) + threadIdx.x / kRowLanes;
+  const int gl = threadIdx.x % kRowLanes;
+  const bool has = rho < nrows;
+  const float T = has ? temp[uint32_t(rho) / uint32_t(P)] : 1.0f;
+  float m;
+  int32_t idx;
+  double s;
+  group_fold(part, rho, has, cpr, gl, T > 0.0f, double(kLog2e / T), m, idx, s);
+  const RowStat st = group_reduce_row(m, idx, s, T);
+  if (has && gl == 0) {
     lnz[rho] = st.lnz;
     if (amax) amax[rho] = st.idx == INT_MAX ? 0 : st.idx;
   }
@@ -1059,10 +1115,10 @@ __global__ __launch_bounds__(kBlock) void given_kernel(ChainArgs a, int64_t chai
 // Per-chain prologue of the step's draw kernel: every split of a chain derives
 // the chain's n itself, so no separate accept launch sits between the stream
 // and the draws. The rows' ln Z come from the stream partials with 8 lanes per
-// row (up to 32 rows per pass of the workgroup, a 3-step reduction per row);
-// the draft-token logits load while the partials fold. Split 0 writes the
+// row (up to 32 rows per pass of the workgroup, a 3-step reduction per row,
+// in the order of group_fold and group_reduce_row, written out here so the
+// draft-token logits load while the partials fold). Split 0 writes the
 // chain's outputs. Returns n in LDS (-1: nothing to draw or an error).
-constexpr int kRowLanes = 8;
 constexpr int kRowsPerPass = kBlock / kRowLanes;
 
 template <int DT>
@@ -2182,9 +2238,9 @@ int specverify_normalize(const void* logits, int dtype, int64_t B, int64_t P, in
   sa.part = part;
   sa.rank_out = nullptr;
   launch_stream(dtype, vec, argmax != nullptr, sa, st);
-  hipLaunchKernelGGL(finalize_rows_kernel,
-                     dim3(unsigned((B * P + kWavesPerBlock - 1) / kWavesPerBlock)), dim3(kBlock), 0,
-                     st, part, B * P, L.cpr, P, temperature, lnZ, argmax);
+  constexpr int kFinRows = kFinBlock / kRowLanes;
+  hipLaunchKernelGGL(finalize_rows_kernel, dim3(unsigned((B * P + kFinRows - 1) / kFinRows)),
+                     dim3(kFinBlock), 0, st, part, B * P, L.cpr, P, temperature, lnZ, argmax);
   return launch_status();
 }
 

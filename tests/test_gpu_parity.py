@@ -171,6 +171,25 @@ def test_normalize_entry_point():
         assert np.all(np.abs(lnz[1:] - rl[1:]) <= 1e-5), np.abs(lnz[1:] - rl[1:]).max()
 
 
+@pytest.mark.parametrize("name,kw", [("c2", {}), ("c3", dict(B=8)), ("c4", dict(B=6))])
+def test_normalize_and_step_give_the_same_normalisers(name, kw):
+    # both fold a row's chunk partials with the same lanes in the same order, so a
+    # caller gets the same ln Z bits from either entry point
+    w = workloads.make(name, **kw)
+    print(f"[case] normalize vs step {name} {kw}", flush=True)
+    t, d = logits_to_dev(w.target, w.dtype), logits_to_dev(w.draft, w.dtype)
+    temp = to_dev(w.temperature)
+    out = sv.specverify_step(t, d, to_dev(w.tokens), temp, w.seed, to_dev(w.pos0))
+    lz_t, am = sv.specverify_normalize(t, temp, want_argmax=True)
+    lz_d, _ = sv.specverify_normalize(d[:, 0], temp)
+    torch.cuda.synchronize()
+    assert torch.equal(lz_t, out.lnZ_target)
+    sampled = torch.from_numpy(w.temperature > 0).to(t.device)
+    assert torch.equal(lz_d[sampled], out.lnZ_draft[:, 0][sampled])
+    want = oracle.normalize_rows(oracle.decode_logits(w.target, w.dtype), w.temperature[:, None])[1]
+    assert np.array_equal(am.cpu().numpy(), want)
+
+
 def test_accept_entry_point_reproduces_the_oracle_exactly():
     rng = np.random.default_rng(3)
     for B, K, g in ((256, 1, 4), (7, 4, 8), (3, 2, 32), (1, 1, 1)):
