@@ -1664,8 +1664,10 @@ __global__ __launch_bounds__(kBlock) void alpha_law_kernel(const OverlapPartial*
 
 constexpr int kTopFBlock = 256;
 constexpr int kTopFCap = 4096;                   // LDS candidate buffer (entries)
-constexpr int kTopFBatch = kTopFBlock * kVec;    // ids scored per pass of the workgroup
+constexpr int kTopFBatch = kTopFBlock * kVec;    // ids admitted per step of the workgroup
 constexpr int kTopFSample = 8;                   // passes sampled for the first threshold
+constexpr int kTopFDepth = 4;                    // vectors per thread loaded one pass ahead
+static_assert(SV_MAX_FANOUT <= kTopFBlock, "the first threshold is one of the threads' maxima");
 
 struct TopFArgs {
   RowSet rs;
@@ -1825,52 +1827,70 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
     }
     if (tid == 0) s_thr = s_max[F - 1];
   }
-  RawVec<DT> nt = neg_inf_vec<DT>(), nd = neg_inf_vec<DT>();
-  if (tid < a.vpr) {
-    nt = load_vec_bounded<DT, VEC>(trow, tid, a.V);
-    if (residual) nd = load_vec_bounded<DT, VEC>(drow, tid, a.V);
+  // kTopFDepth vectors per thread per pass, the next pass's loaded while this
+  // one is scored; each vector's ids are admitted (and the buffer cut) in turn,
+  // so the ids go through in the order of one vector per thread per step.
+  constexpr int64_t kPass = int64_t(kTopFBlock) * kTopFDepth;
+  RawVec<DT> nt[kTopFDepth], nd[kTopFDepth];
+#pragma unroll
+  for (int u = 0; u < kTopFDepth; ++u) {
+    const int64_t vi = int64_t(u) * kTopFBlock + tid;
+    nt[u] = neg_inf_vec<DT>();
+    nd[u] = nt[u];
+    if (vi < a.vpr) {
+      nt[u] = load_vec_bounded<DT, VEC>(trow, vi, a.V);
+      if (residual) nd[u] = load_vec_bounded<DT, VEC>(drow, vi, a.V);
+    }
   }
   __syncthreads();
-  for (int64_t base = 0; base < a.vpr; base += kTopFBlock) {
-    const int64_t vi = base + tid;
-    const RawVec<DT> rt = nt;
-    const RawVec<DT> rd = nd;
-    const int64_t vn = vi + kTopFBlock;
-    if (vn < a.vpr) {
-      nt = load_vec_bounded<DT, VEC>(trow, vn, a.V);
-      if (residual) nd = load_vec_bounded<DT, VEC>(drow, vn, a.V);
-    }
-    float sc[kVec];
+  for (int64_t pbase = 0; pbase < a.vpr; pbase += kPass) {
+    RawVec<DT> ct[kTopFDepth], cd[kTopFDepth];
 #pragma unroll
-    for (int t = 0; t < kVec; ++t) sc[t] = vi < a.vpr ? score_at(rt, rd, t) : -INFINITY;
-    const float thr = s_thr;
-    int mine = 0;
-#pragma unroll
-    for (int t = 0; t < kVec; ++t) {
-      const bool keep = sc[t] > -INFINITY && sc[t] >= thr;
-      sc[t] = keep ? sc[t] : -INFINITY;
-      mine += keep ? 1 : 0;
-    }
-    if (mine) {
-      int slot = atomicAdd(&s_cnt, mine);
-#pragma unroll
-      for (int t = 0; t < kVec; ++t)
-        if (sc[t] > -INFINITY) {
-          sw[slot] = sc[t];
-          si[slot] = int32_t(vi * kVec + t);
-          ++slot;
-        }
-    }
-    lds_barrier();
-    const int cnt = s_cnt;
-    if (cnt > kTopFCap - kTopFBatch || cnt > 256) {  // cut to the best F
-      topf_sort(sw, si, cnt);
-      if (tid == 0) {
-        s_cnt = cnt < F ? cnt : F;
-        if (cnt >= F && sw[F - 1] > s_thr) s_thr = sw[F - 1];
+    for (int u = 0; u < kTopFDepth; ++u) {
+      ct[u] = nt[u];
+      cd[u] = nd[u];
+      const int64_t vn = pbase + kPass + int64_t(u) * kTopFBlock + tid;
+      if (vn < a.vpr) {
+        nt[u] = load_vec_bounded<DT, VEC>(trow, vn, a.V);
+        if (residual) nd[u] = load_vec_bounded<DT, VEC>(drow, vn, a.V);
       }
     }
-    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < kTopFDepth; ++u) {
+      const int64_t vi = pbase + int64_t(u) * kTopFBlock + tid;
+      if (pbase + int64_t(u) * kTopFBlock >= a.vpr) break;   // uniform: the row has ended
+      float sc[kVec];
+#pragma unroll
+      for (int t = 0; t < kVec; ++t) sc[t] = vi < a.vpr ? score_at(ct[u], cd[u], t) : -INFINITY;
+      const float thr = s_thr;
+      int mine = 0;
+#pragma unroll
+      for (int t = 0; t < kVec; ++t) {
+        const bool keep = sc[t] > -INFINITY && sc[t] >= thr;
+        sc[t] = keep ? sc[t] : -INFINITY;
+        mine += keep ? 1 : 0;
+      }
+      if (mine) {
+        int slot = atomicAdd(&s_cnt, mine);
+#pragma unroll
+        for (int t = 0; t < kVec; ++t)
+          if (sc[t] > -INFINITY) {
+            sw[slot] = sc[t];
+            si[slot] = int32_t(vi * kVec + t);
+            ++slot;
+          }
+      }
+      lds_barrier();
+      const int cnt = s_cnt;
+      if (cnt > kTopFCap - kTopFBatch || cnt > 256) {  // cut to the best F
+        topf_sort(sw, si, cnt);
+        if (tid == 0) {
+          s_cnt = cnt < F ? cnt : F;
+          if (cnt >= F && sw[F - 1] > s_thr) s_thr = sw[F - 1];
+        }
+      }
+      lds_barrier();
+    }
   }
   const int cnt = s_cnt;
   topf_sort(sw, si, cnt);
