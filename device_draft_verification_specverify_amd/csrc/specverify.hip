@@ -1664,7 +1664,10 @@ __global__ __launch_bounds__(kBlock) void alpha_law_kernel(const OverlapPartial*
 
 constexpr int kTopFBlock = 256;
 constexpr int kTopFCap = 4096;                   // LDS candidate buffer (entries)
-constexpr int kTopFBatch = kTopFBlock * kVec;    // ids admitted per step of the workgroup
+constexpr int kTopFWaves = kTopFBlock / kWave;
+constexpr int kTopFWaveCap = kTopFCap / kTopFWaves;  // one wavefront's region of the buffer
+constexpr int kTopFCut = 256;                    // a region past this many entries is cut
+static_assert(kTopFCut + kWave * kVec <= kTopFWaveCap, "a step's admissions fit a region");
 constexpr int kTopFSample = 8;                   // passes sampled for the first threshold
 constexpr int kTopFDepth = 4;                    // vectors per thread loaded one pass ahead
 static_assert(SV_MAX_FANOUT <= kTopFBlock, "the first threshold is one of the threads' maxima");
@@ -1722,10 +1725,51 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Orders one wavefront's LDS accesses: its earlier ones complete before any
+// later one issues (for data handed between its own lanes).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// topf_sort for the n <= kTopFWaveCap entries of one wavefront's region, by
+// that wavefront alone (no workgroup barrier).
+__device__ void topf_wave_sort(float* sw, int32_t* si, int n) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  for (int i = n + lane; i < n2; i += kWave) {
+    sw[i] = -INFINITY;
+    si[i] = INT_MAX;
+  }
+  wave_lds_sync();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = lane; i < n2; i += kWave) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const bool first = (i & k) == 0;
+          const bool later_is_better = topf_before(sw[ixj], si[ixj], sw[i], si[i]);
+          if (later_is_better == first) {
+            const float tw = sw[i];
+            const int32_t ti = si[i];
+            sw[i] = sw[ixj];
+            si[i] = si[ixj];
+            sw[ixj] = tw;
+            si[ixj] = ti;
+          }
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
 // One workgroup per (chain, outcome j) with F_j > 0. A streaming selection:
-// ids whose score reaches the current threshold go to an LDS buffer; past 256
-// entries the buffer is sorted, cut to the best F_j, and the threshold becomes
-// the F_j-th score. The first threshold is the F_j-th largest of the threads'
+// ids whose score reaches the current threshold go to their wavefront's region
+// of an LDS buffer (slots from ballots); past 256 entries a wavefront sorts its
+// region, cuts it to the best F_j and raises its threshold to the F_j-th score,
+// without waiting for the others; at the end the regions are merged and sorted. The first threshold is the F_j-th largest of the threads'
 // maxima over a sample of passes spread over the row (F_j distinct ids reach
 // it, so it is no higher than the row's F_j-th score). The next pass's vectors load while the
 // current one is scored. Scores: residual or target weights in float32 (the
@@ -1736,7 +1780,7 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
   __shared__ float sw[kTopFCap];
   __shared__ int32_t si[kTopFCap];
   __shared__ float s_max[kTopFBlock];
-  __shared__ int s_cnt;
+  __shared__ int s_wcnt[kTopFWaves];
   __shared__ float s_thr;
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   const RowSet& rs = a.rs;
@@ -1774,7 +1818,6 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
   const float c_lo = float(l2t - double(c_hi));
   const float d2 = residual ? float((a.lnz_t[b * (G + 1) + j] - a.lnz_d[chain * G + j]) * kLog2eD)
                             : 0.0f;
-  if (tid == 0) s_cnt = 0;
   // The weight (float32 score) of id vi*8+t; -inf: not a candidate.
   auto score_at = [&](const RawVec<DT>& rt, const RawVec<DT>& rd, int t) {
     const float zt = vec_elem<DT>(rt, t);
@@ -1843,6 +1886,16 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
     }
   }
   __syncthreads();
+  // Each wavefront admits into its own region with its own threshold (the
+  // sampled one, raised to its region's F-th score at each cut): an id below
+  // it has F better ids in that region, so the union of the regions' best F
+  // holds the row's best F.
+  const int wv = tid / kWave;
+  const int lane = tid % kWave;
+  float* rw = sw + wv * kTopFWaveCap;
+  int32_t* ri = si + wv * kTopFWaveCap;
+  int wcnt = 0;
+  float thr = s_thr;
   for (int64_t pbase = 0; pbase < a.vpr; pbase += kPass) {
     RawVec<DT> ct[kTopFDepth], cd[kTopFDepth];
 #pragma unroll
@@ -1862,37 +1915,47 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
       float sc[kVec];
 #pragma unroll
       for (int t = 0; t < kVec; ++t) sc[t] = vi < a.vpr ? score_at(ct[u], cd[u], t) : -INFINITY;
-      const float thr = s_thr;
-      int mine = 0;
+      // admit into this wavefront's region: slots from ballots, no atomics
+      int base = wcnt;
 #pragma unroll
       for (int t = 0; t < kVec; ++t) {
         const bool keep = sc[t] > -INFINITY && sc[t] >= thr;
-        sc[t] = keep ? sc[t] : -INFINITY;
-        mine += keep ? 1 : 0;
-      }
-      if (mine) {
-        int slot = atomicAdd(&s_cnt, mine);
-#pragma unroll
-        for (int t = 0; t < kVec; ++t)
-          if (sc[t] > -INFINITY) {
-            sw[slot] = sc[t];
-            si[slot] = int32_t(vi * kVec + t);
-            ++slot;
-          }
-      }
-      lds_barrier();
-      const int cnt = s_cnt;
-      if (cnt > kTopFCap - kTopFBatch || cnt > 256) {  // cut to the best F
-        topf_sort(sw, si, cnt);
-        if (tid == 0) {
-          s_cnt = cnt < F ? cnt : F;
-          if (cnt >= F && sw[F - 1] > s_thr) s_thr = sw[F - 1];
+        const uint64_t bal = __ballot(keep);
+        if (keep) {
+          const int slot = base + int(__builtin_amdgcn_mbcnt_hi(
+                                      uint32_t(bal >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0u)));
+          rw[slot] = sc[t];
+          ri[slot] = int32_t(vi * kVec + t);
         }
+        base += __popcll(bal);
       }
-      lds_barrier();
+      wcnt = base;
+      if (wcnt > kTopFCut) {  // uniform in the wavefront: cut its region to the best F
+        wave_lds_sync();
+        topf_wave_sort(rw, ri, wcnt);
+        if (wcnt >= F) {
+          const float f = rw[F - 1];
+          if (f > thr) thr = f;
+        }
+        wcnt = wcnt < F ? wcnt : F;
+      }
     }
   }
-  const int cnt = s_cnt;
+  // merge the regions: each wavefront moves its entries behind the earlier ones'
+  if (lane == 0) s_wcnt[wv] = wcnt;
+  __syncthreads();
+  int off = 0, cnt = 0;
+#pragma unroll
+  for (int w = 0; w < kTopFWaves; ++w) {
+    off += w < wv ? s_wcnt[w] : 0;
+    cnt += s_wcnt[w];
+  }
+  if (wv > 0)
+    for (int i = lane; i < wcnt; i += kWave) {
+      sw[off + i] = rw[i];
+      si[off + i] = ri[i];
+    }
+  __syncthreads();
   topf_sort(sw, si, cnt);
   for (int i = tid; i < F; i += kTopFBlock) {
     const bool have = i < cnt;
