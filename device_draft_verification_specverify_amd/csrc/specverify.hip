@@ -1915,21 +1915,30 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
       float sc[kVec];
 #pragma unroll
       for (int t = 0; t < kVec; ++t) sc[t] = vi < a.vpr ? score_at(ct[u], cd[u], t) : -INFINITY;
-      // admit into this wavefront's region: slots from ballots, no atomics
-      int base = wcnt;
+      // admit into this wavefront's region: slots from ballots, no atomics;
+      // most steps admit nothing anywhere in the wavefront and skip it all
+      bool keep[kVec];
+      bool any = false;
 #pragma unroll
       for (int t = 0; t < kVec; ++t) {
-        const bool keep = sc[t] > -INFINITY && sc[t] >= thr;
-        const uint64_t bal = __ballot(keep);
-        if (keep) {
-          const int slot = base + int(__builtin_amdgcn_mbcnt_hi(
-                                      uint32_t(bal >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0u)));
-          rw[slot] = sc[t];
-          ri[slot] = int32_t(vi * kVec + t);
-        }
-        base += __popcll(bal);
+        keep[t] = sc[t] > -INFINITY && sc[t] >= thr;
+        any = any || keep[t];
       }
-      wcnt = base;
+      if (__any(any)) {
+        int base = wcnt;
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) {
+          const uint64_t bal = __ballot(keep[t]);
+          if (keep[t]) {
+            const int slot = base + int(__builtin_amdgcn_mbcnt_hi(
+                                        uint32_t(bal >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0u)));
+            rw[slot] = sc[t];
+            ri[slot] = int32_t(vi * kVec + t);
+          }
+          base += __popcll(bal);
+        }
+        wcnt = base;
+      }
       if (wcnt > kTopFCut) {  // uniform in the wavefront: cut its region to the best F
         wave_lds_sync();
         topf_wave_sort(rw, ri, wcnt);
