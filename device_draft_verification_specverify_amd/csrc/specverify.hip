@@ -1913,8 +1913,34 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
       const int64_t vi = pbase + int64_t(u) * kTopFBlock + tid;
       if (pbase + int64_t(u) * kTopFBlock >= a.vpr) break;   // uniform: the row has ended
       float sc[kVec];
+      if (residual) {
+        // w = 2^a2 minus a non-negative term, so w <= 2^a2 exactly: unless an
+        // id of the wavefront has 2^a2 at the threshold, none can be admitted
+        // and the draft term is skipped (the same operations as score_at)
+        float a2[kVec], e1[kVec];
+        bool need = false;
 #pragma unroll
-      for (int t = 0; t < kVec; ++t) sc[t] = vi < a.vpr ? score_at(ct[u], cd[u], t) : -INFINITY;
+        for (int t = 0; t < kVec; ++t) {
+          const float zt = vec_elem<DT>(ct[u], t);
+          a2[t] = fmaf(zt, k_hi, -c_hi) + fmaf(zt, k_lo, -c_lo);
+          e1[t] = __builtin_amdgcn_exp2f(a2[t]);
+          need = need || e1[t] >= thr;
+        }
+        if (__any(need && vi < a.vpr)) {
+#pragma unroll
+          for (int t = 0; t < kVec; ++t) {
+            const float zt = vec_elem<DT>(ct[u], t);
+            const float w = e1[t] - __builtin_amdgcn_exp2f(a2[t] + fmaf(vec_elem<DT>(cd[u], t) - zt, k_hi, d2));
+            sc[t] = vi < a.vpr && w > 0.0f ? w : -INFINITY;
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < kVec; ++t) sc[t] = -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kVec; ++t) sc[t] = vi < a.vpr ? score_at(ct[u], cd[u], t) : -INFINITY;
+      }
       // admit into this wavefront's region: slots from ballots, no atomics;
       // most steps admit nothing anywhere in the wavefront and skip it all
       bool keep[kVec];
