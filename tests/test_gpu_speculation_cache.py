@@ -133,6 +133,26 @@ def test_topf_greedy_ties_and_invalid_temperature():
     assert np.all(c2[1] == -1) and np.all(c2[0] >= 0)
 
 
+def test_topf_massive_ties_cut_every_wavefront_region():
+    # z_t = 0 everywhere and z_d = -10 except on every 7th id (+10, no residual mass
+    # there): the residual weight is the same float on 6 ids of 7 and the bonus
+    # weight on every id, so each wavefront admits ~440 ids a step and cuts its
+    # region every step; the best F are then exactly the lowest ids
+    w = workloads.make("c3", B=2, V=40000, gamma=2, temps=("const", 1.0))
+    w.target[:] = np.uint16(0x0000)
+    w.draft[:] = np.uint16(0xC120)
+    w.draft[..., ::7] = np.uint16(0x4120)
+    fan = [64, 64, 64]
+    print(f"[case] topf massive ties V={w.V} fan={fan}", flush=True)
+    cand, _, slot, n, y = _run(w, fan)
+    ref, _ = sc.residual_topf(w.target, w.draft, w.temperature, fan, dtype=w.dtype)
+    want_res = np.array([v for v in range(200) if v % 7][:64])
+    assert np.array_equal(ref[0, 0, :64], want_res)          # the reading the oracle fixes
+    assert np.array_equal(ref[0, 0, 128:], np.arange(64))
+    assert np.array_equal(cand, ref)
+    _compare(w, fan, cand, slot, n, y)
+
+
 def test_hit_rate_tracks_the_law_on_the_gpu():
     # many replicate chains of one batch row: the GPU cache hit rate over the GPU step's
     # outcomes matches the rate the oracle predicts from alpha and the residual masses
