@@ -1669,6 +1669,8 @@ constexpr int kTopFWaveCap = kTopFCap / kTopFWaves;  // one wavefront's region o
 constexpr int kTopFCut = 256;                    // a region past this many entries is cut
 static_assert(kTopFCut + kWave * kVec <= kTopFWaveCap, "a step's admissions fit a region");
 constexpr int kTopFSample = 8;                   // passes sampled for the first threshold
+constexpr int kTopFSampleWide = 16;              // ... when the grid is 1 to 8 workgroups per CU
+constexpr int kTopFWideRowsPerCU = 8;
 constexpr int kTopFDepth = 4;                    // vectors per thread loaded one pass ahead
 static_assert(SV_MAX_FANOUT <= kTopFBlock, "the first threshold is one of the threads' maxima");
 
@@ -1769,13 +1771,15 @@ __device__ void topf_wave_sort(float* sw, int32_t* si, int n) {
 // ids whose score reaches the current threshold go to their wavefront's region
 // of an LDS buffer (slots from ballots); past 256 entries a wavefront sorts its
 // region, cuts it to the best F_j and raises its threshold to the F_j-th score,
-// without waiting for the others; at the end the regions are merged and sorted. The first threshold is the F_j-th largest of the threads'
-// maxima over a sample of passes spread over the row (F_j distinct ids reach
-// it, so it is no higher than the row's F_j-th score). The next pass's vectors load while the
-// current one is scored. Scores: residual or target weights in float32 (the
-// exponent split in two floats so that large z/T costs no precision), raw
-// logits for greedy rows; -inf = not a candidate.
-template <int DT, bool VEC>
+// without waiting for the others; at the end the regions are merged and
+// sorted. The first threshold is the F_j-th largest of the threads' maxima
+// over a sample of passes spread over the row (F_j distinct ids reach it, so
+// it is no higher than the row's F_j-th score). The next pass's vectors load
+// while the current one is scored. Scores: residual or target weights in
+// float32 (the exponent split in two floats so that large z/T costs no
+// precision; a residual's draft term only where the target term reaches the
+// threshold), raw logits for greedy rows; -inf = not a candidate.
+template <int DT, bool VEC, int NS>
 __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
   __shared__ float sw[kTopFCap];
   __shared__ int32_t si[kTopFCap];
@@ -1828,16 +1832,16 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
     return w > 0.0f ? w : -INFINITY;
   };
   // First threshold: the F-th largest of the threads' maxima over a sample of
-  // kTopFSample passes spread evenly over the row. The sampled ids are
+  // NS passes spread evenly over the row. The sampled ids are
   // distinct, so at least F of them reach it and it is no higher than the
   // row's F-th weight; being taken over the whole row, it admits far fewer
   // ids than the first pass alone would (fewer sorts of the buffer).
   {
     const int64_t passes = (a.vpr + kTopFBlock - 1) / kTopFBlock;
-    const int64_t pstride = passes > kTopFSample ? passes / kTopFSample : 1;
-    RawVec<DT> st[kTopFSample], sd[kTopFSample];
+    const int64_t pstride = passes > NS ? passes / NS : 1;
+    RawVec<DT> st[NS], sd[NS];
 #pragma unroll
-    for (int i = 0; i < kTopFSample; ++i) {
+    for (int i = 0; i < NS; ++i) {
       const int64_t vi = int64_t(i) * pstride * kTopFBlock + tid;
       st[i] = neg_inf_vec<DT>();
       sd[i] = st[i];
@@ -1848,7 +1852,7 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kTopFSample; ++i)
+    for (int i = 0; i < NS; ++i)
 #pragma unroll
       for (int t = 0; t < kVec; ++t) mx = fmaxf(mx, score_at(st[i], sd[i], t));
     s_max[tid] = mx;
@@ -2100,6 +2104,24 @@ Layout make_layout(int64_t B, int64_t nrows, int64_t chains, int64_t V, int dtyp
   return L;
 }
 
+// Compute units of the current device (cached per device; only speed
+// depends on it).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 // Workgroups of one stream-kernel instantiation resident on the device at
 // once: the persistent grid (cached per device; only speed depends on it).
 template <int DT, bool VEC, bool ARGMAX_ALL>
@@ -2310,6 +2332,14 @@ bool fill_fanout(const int32_t* fan, int64_t G, TopFArgs& a) {
   a.off[G + 1] = int32_t(off);
   a.ftot = off;
   return true;
+}
+
+template <int DT, bool VEC>
+void launch_topf(bool wide, dim3 grid, hipStream_t st, const TopFArgs& ta) {
+  if (wide)
+    hipLaunchKernelGGL((topf_kernel<DT, VEC, kTopFSampleWide>), grid, dim3(kTopFBlock), 0, st, ta);
+  else
+    hipLaunchKernelGGL((topf_kernel<DT, VEC, kTopFSample>), grid, dim3(kTopFBlock), 0, st, ta);
 }
 
 }  // namespace
@@ -2613,13 +2643,20 @@ int specverify_residual_topf(const void* target_logits, const void* draft_logits
   ta.cand = cand;
   ta.cand_w = cand_weight;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid{unsigned(B * K * (gamma + 1)), 1u, 1u};
+  const int64_t rows = B * K * (gamma + 1);
+  const dim3 grid{unsigned(rows), 1u, 1u};
+  // A wider sample gives a tighter first threshold (fewer admissions) for
+  // twice the sample loads and more registers: it pays while the grid holds
+  // one to a few workgroups per CU; below that the kernel is one workgroup's
+  // latency, above it occupancy bounds the rate.
+  const int64_t cus = device_cus();
+  const bool wide = rows >= cus && rows <= int64_t(kTopFWideRowsPerCU) * cus;
   if (dtype == SV_BF16) {
-    if (vec) hipLaunchKernelGGL((topf_kernel<SV_BF16, true>), grid, dim3(kTopFBlock), 0, st, ta);
-    else hipLaunchKernelGGL((topf_kernel<SV_BF16, false>), grid, dim3(kTopFBlock), 0, st, ta);
+    if (vec) launch_topf<SV_BF16, true>(wide, grid, st, ta);
+    else launch_topf<SV_BF16, false>(wide, grid, st, ta);
   } else {
-    if (vec) hipLaunchKernelGGL((topf_kernel<SV_F32, true>), grid, dim3(kTopFBlock), 0, st, ta);
-    else hipLaunchKernelGGL((topf_kernel<SV_F32, false>), grid, dim3(kTopFBlock), 0, st, ta);
+    if (vec) launch_topf<SV_F32, true>(wide, grid, st, ta);
+    else launch_topf<SV_F32, false>(wide, grid, st, ta);
   }
   return launch_status();
 }

@@ -133,6 +133,16 @@ def test_topf_greedy_ties_and_invalid_temperature():
     assert np.all(c2[1] == -1) and np.all(c2[0] >= 0)
 
 
+def test_topf_large_grid_takes_the_narrow_sample():
+    # 512 x 6 = 3072 rows, more than 8 per CU: the launch samples 8 passes (not the
+    # 16 of grids with 1 to 8 rows per CU, such as the full C3 case above)
+    w = workloads.make("c2", B=512, V=8000)
+    fan = sv.geometric_fanout(w.gamma, 24, 0.7)
+    print(f"[case] topf large grid B={w.B} V={w.V} fan={fan}", flush=True)
+    cand, _, slot, n, y = _run(w, fan)
+    _compare(w, fan, cand, slot, n, y, rows=np.arange(0, 512, 16))
+
+
 def test_topf_massive_ties_cut_every_wavefront_region():
     # z_t = 0 everywhere and z_d = -10 except on every 7th id (+10, no residual mass
     # there): the residual weight is the same float on 6 ids of 7 and the bonus
