@@ -1875,8 +1875,8 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
     if (tid == 0) s_thr = s_max[F - 1];
   }
   // kTopFDepth vectors per thread per pass, the next pass's loaded while this
-  // one is scored; each vector's ids are admitted (and the buffer cut) in turn,
-  // so the ids go through in the order of one vector per thread per step.
+  // one is scored; each vector's ids are admitted (and the wavefront's region
+  // cut) in turn, so a step adds at most one vector per lane to a region.
   constexpr int64_t kPass = int64_t(kTopFBlock) * kTopFDepth;
   RawVec<DT> nt[kTopFDepth], nd[kTopFDepth];
 #pragma unroll
