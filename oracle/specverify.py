@@ -30,6 +30,8 @@ Readings where the pages are silent (each is listed in the design doc):
 * the draft distribution uses the same per-row temperature as the target;
 * an empty residual support (reachable only through rounding) falls back to a
   draw from p_n with the same noise;
+* a needed row whose largest logit is not finite (every entry -inf, or any
+  +inf or NaN entry) is an input error of its chains;
 * decisions after the first rejection are computed but do not matter;
 * greedy rows report ln Z_t = max_v z (the T -> 0 limit of T * ln Z),
   ln p in {0, -inf} and ln q = 0, so the scalar accept test reproduces them;
@@ -50,7 +52,7 @@ FLAG_EPS = 1e-6
 
 ERR_TOKEN = 1   # a draft token outside [0, V)
 ERR_TEMP = 2    # temperature negative or NaN
-ERR_ROW = 4     # a needed row whose largest logit is -inf or NaN
+ERR_ROW = 4     # a needed row whose largest logit is not finite: all -inf, +inf or NaN
 
 
 def decode_logits(raw, dtype: str) -> np.ndarray:
@@ -205,16 +207,24 @@ def sample_tokens(target, draft, T, lnz_t, lnz_d, argmax_t, n, seed: int, pos0, 
         no_support = np.all(np.isneginf(logr), axis=-1)
         scores = np.where(no_support[:, None], lp + G, logr + G)
         y = gumbel_argmax(scores)
+        rows = np.arange(len(y))
         # Robustness of the draw: each difference lq - lp and each score may be off by eps.
         with np.errstate(invalid="ignore"):
             d = lq - lp
             hi = lp + _residual_factor(d - eps) + G + eps
-            rows = np.arange(len(y))
             lo_y = lp[rows, y] + _residual_factor(d[rows, y] + eps) + G[rows, y] - eps
             hi[rows, y] = -np.inf
             fl = np.max(hi, axis=-1) >= lo_y
+            # Empty support (the draw from p_n): the emptiness itself is fragile when some
+            # id sits within eps of the support (lq - lp < eps), and the draw from p_n is
+            # fragile when its runner-up is within 2 eps, as for the bonus draw.
+            near = np.any(d < eps, axis=-1)
+            ps = lp + G
+            best = ps[rows, y]
+            ps[rows, y] = -np.inf
+            fl_empty = near | (np.max(ps, axis=-1) >= best - 2 * eps)
         token[res] = y
-        flagged[res] = fl | no_support
+        flagged[res] = np.where(no_support, fl_empty, fl)
         empty[res] = no_support
 
     bon = (T[bb] > 0) & (n == g)
@@ -296,9 +306,9 @@ def verify(target, draft, tokens, temperature, seed: int, pos0, batch_index=None
     err_chain |= np.where(~tok_ok.all(axis=-1), ERR_TOKEN, 0)
     err_chain |= np.where(~(sampled | greedy), ERR_TEMP, 0)[:, None]
     tmax = np.max(target, axis=-1)
-    bad_t = np.any(~(tmax > -np.inf), axis=-1)          # -inf or NaN maximum
+    bad_t = np.any(~np.isfinite(tmax), axis=-1)         # -inf, +inf or NaN maximum
     dmax = np.max(draft, axis=-1)
-    bad_d = np.any(~(dmax > -np.inf), axis=-1) & sampled[:, None]
+    bad_d = np.any(~np.isfinite(dmax), axis=-1) & sampled[:, None]
     err_chain |= np.where(bad_t[:, None] | bad_d, ERR_ROW, 0)
     bad = err_chain != 0
     accept_len = np.where(bad, -1, n)
