@@ -125,7 +125,7 @@ def workspace(B: int, K: int, gamma: int, V: int, dtype: int, device) -> torch.T
     n = workspace_size(B, K, gamma, V, dtype)
     if n == 0:
         raise SpecVerifyError("sizes rejected by specverify_workspace_size")
-    return torch.zeros(n, dtype=torch.uint8, device=device)  # zero before first use
+    return torch.empty(n, dtype=torch.uint8, device=device)  # any contents will do
 
 
 def specverify_normalize(logits: torch.Tensor, temperature: torch.Tensor, want_argmax: bool = False,
@@ -247,19 +247,21 @@ class StepPlan:
                        if want_normalizers else None),
             device_error=torch.zeros(1, dtype=torch.int32, device=dev) if want_error else None,
         )
-        self.ws = ws if ws is not None else workspace(B, K, g, V, self.dtype, dev)
         o = self.out
         self._args = (
             target.data_ptr(), draft.data_ptr(), self.dtype, tokens.data_ptr(), B, K, g, V,
             target.stride(0), target.stride(1), draft.stride(0), draft.stride(1), draft.stride(2),
             temperature.data_ptr(), self.seed, _ptr(pos0), o.accept_len.data_ptr(),
             o.out_token.data_ptr(), _ptr(o.logp), _ptr(o.logq), _ptr(o.lnZ_target),
-            _ptr(o.lnZ_draft), _ptr(o.device_error), self.ws.data_ptr(), self.ws.numel())
+            _ptr(o.lnZ_draft), _ptr(o.device_error))
+        self.ws = ws if ws is not None else workspace(B, K, g, V, self.dtype, dev)
+        self._args += (self.ws.data_ptr(), self.ws.numel())
+        self._fn, self._name = self.lib.specverify_step, "specverify_step"
         self.device = dev
 
     def __call__(self, stream: int | None = None) -> StepOutputs:
-        st = self.lib.specverify_step(*self._args, _stream(self.device) if stream is None else stream)
-        _check(st, "specverify_step")
+        st = self._fn(*self._args, _stream(self.device) if stream is None else stream)
+        _check(st, self._name)
         return self.out
 
 

@@ -204,6 +204,22 @@ __device__ __forceinline__ float vec_elem(const RawVec<DT>& r, int t) {
   }
 }
 
+// Nonzero when some slot of the vector holds a NaN, from the raw bits: with
+// the sign cleared a bf16 half (or an f32 word) is a NaN iff it exceeds the
+// +inf pattern 0x7F80 (0x7F800000), i.e. iff adding 0x7F (0x7FFFFF) carries
+// into its top bit; the low half's sum stays below 2^16, so the halves of a
+// word do not interact. Integer ops on packed words, no unpacking.
+template <int DT>
+__device__ __forceinline__ uint32_t nan_bits(const RawVec<DT>& r) {
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < (DT == SV_BF16 ? 4 : 8); ++i) {
+    if constexpr (DT == SV_BF16) acc |= ((r.w[i] & 0x7FFF7FFFu) + 0x007F007Fu) & 0x80008000u;
+    else acc |= ((r.w[i] & 0x7FFFFFFFu) + 0x007FFFFFu) & 0x80000000u;
+  }
+  return acc;
+}
+
 // A vector that reads -inf in every slot.
 template <int DT>
 __device__ __forceinline__ RawVec<DT> neg_inf_vec() {
@@ -275,6 +291,7 @@ struct RowStat {
   double lnz;
   float m;
   int32_t idx;
+  bool bad;  // the row is an input error (row_bad)
 };
 
 // 2^e for a rescaling exponent e <= 0 between partial sums, in single
@@ -284,73 +301,39 @@ __device__ __forceinline__ double exp2_scale(double e) {
 }
 
 // Fold chunk partial q into a lane's running (m, idx, s); s stays relative to
-// m in units of k2 = float(log2(e) / T).
+// m in units of k2 = float(log2(e) / T). A partial whose maximum is -inf, and
+// every partial of a greedy row, carries s = 0, or NaN when its chunk held a
+// NaN; that s is added as it is, so a NaN anywhere in a row reaches the row's
+// sum (a +inf logit makes its chunk's sum NaN too).
 __device__ __forceinline__ void fold_partial(float& m, int32_t& idx, double& s, const RowPartial& q,
                                              bool sampled, double k2) {
   float bm = m;
   int32_t bi = idx;
   better_max(bm, bi, q.m, q.idx);
-  if (sampled && bm > -INFINITY) {
-    if (m > -INFINITY) s *= exp2_scale((double(m) - double(bm)) * k2);
-    if (q.m != -INFINITY) s += q.s * exp2_scale((double(q.m) - double(bm)) * k2);
+  if (sampled) {
+    if (bm > -INFINITY && m > -INFINITY) s *= exp2_scale((double(m) - double(bm)) * k2);
+    s += q.m > -INFINITY ? q.s * exp2_scale((double(q.m) - double(bm)) * k2) : q.s;
+  } else {
+    s += q.s;
   }
   m = bm;
   idx = bi;
 }
 
-// Statistics of NR stream rows (rho[r] < 0: none) by one wavefront: lane l
-// folds chunks l, l + 64, ... of each row, the loads of all NR rows issued
-// together; wave_reduce_row then combines the lanes of one row, and every lane
-// gets the result. lnZ: ln sum exp(z / T) for T > 0, the raw maximum for
-// T == 0, NaN otherwise (an all -inf row gives -inf).
-template <int NR>
-__device__ __forceinline__ void lane_fold(const RowPartial* __restrict__ part,
-                                          const int64_t (&rho)[NR], int64_t cpr, float T,
-                                          float (&m)[NR], int32_t (&idx)[NR], double (&s)[NR]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const bool sampled = T > 0.0f;
-  const double k2 = double(kLog2e / T);
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    m[r] = -INFINITY;
-    idx[r] = INT_MAX;
-    s[r] = 0.0;
-  }
-  for (int64_t c = lane; c < cpr; c += kWave) {
-    RowPartial q[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-      q[r] = rho[r] >= 0 ? part[rho[r] * cpr + c] : RowPartial{-INFINITY, INT_MAX, 0.0};
-#pragma unroll
-    for (int r = 0; r < NR; ++r) fold_partial(m[r], idx[r], s[r], q[r], sampled, k2);
-  }
+// A needed row is an input error when its largest logit is not finite (every
+// entry -inf, or a +inf) or it holds a NaN (its folded sum is NaN).
+__device__ __forceinline__ bool row_bad(float M, double sr) {
+  return !(M > -INFINITY && M < INFINITY && sr == sr);
 }
 
-// Combine the lanes' (m, idx, s) of one row in a fixed order.
-__device__ __forceinline__ RowStat wave_reduce_row(float m, int32_t idx, double s, float T) {
-  const bool sampled = T > 0.0f;
-  const double k2 = double(kLog2e / T);
-  float M = m;
-  int32_t I = idx;
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const float om = __shfl_xor(M, off, kWave);
-    const int32_t oi = __shfl_xor(I, off, kWave);
-    better_max(M, I, om, oi);
-  }
-  double sr = 0.0;
-  if (sampled && M > -INFINITY) {
-    sr = m > -INFINITY ? s * exp2_scale((double(m) - double(M)) * k2) : 0.0;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
-  }
-  RowStat out;
-  out.m = M;
-  out.idx = I;
-  if (sampled) out.lnz = M > -INFINITY ? double(M) / double(T) + log(sr) : double(M);
-  else if (T == 0.0f) out.lnz = double(M);
-  else out.lnz = NAN;
-  return out;
+// ln Z of a row from its maximum M and its folded sum sr (relative to M):
+// ln sum exp(z / T) for T > 0, max z for T == 0, NaN for other T and for rows
+// holding a NaN or (T > 0) a +inf; an all -inf row gives -inf.
+__device__ __forceinline__ double row_lnz(float M, double sr, float T) {
+  if (!(sr == sr)) return NAN;
+  if (T > 0.0f) return M > -INFINITY ? double(M) / double(T) + log(sr) : double(M);
+  if (T == 0.0f) return double(M);
+  return NAN;
 }
 
 // Statistics of one stream row by a group of kRowLanes consecutive lanes, for
@@ -359,8 +342,7 @@ __device__ __forceinline__ RowStat wave_reduce_row(float m, int32_t idx, double 
 // group_reduce_row combines the group in a fixed order (xor 4, 2, 1). The
 // draws' prologue folds and combines its rows in this same order, inline, so
 // that both give a row the same bits. Every lane of the wavefront calls
-// group_reduce_row; all lanes of a group get the result, with lnZ as for
-// wave_reduce_row.
+// group_reduce_row; all lanes of a group get the result (lnZ as row_lnz).
 constexpr int kRowLanes = 8;
 
 __device__ __forceinline__ void group_fold(const RowPartial* __restrict__ part, int64_t rho,
@@ -392,16 +374,14 @@ __device__ __forceinline__ RowStat group_reduce_row(float m, int32_t idx, double
     const int32_t oi = __shfl_xor(I, off, kWave);
     better_max(M, I, om, oi);
   }
-  double sr = 0.0;
-  if (sampled && M > -INFINITY) sr = m > -INFINITY ? s * exp2_scale((double(m) - double(M)) * k2) : 0.0;
+  double sr = (sampled && M > -INFINITY && m > -INFINITY) ? s * exp2_scale((double(m) - double(M)) * k2) : s;
 #pragma unroll
   for (int off = kRowLanes / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
   RowStat out;
   out.m = M;
   out.idx = I;
-  if (sampled) out.lnz = M > -INFINITY ? double(M) / double(T) + log(sr) : double(M);
-  else if (T == 0.0f) out.lnz = double(M);
-  else out.lnz = NAN;
+  out.lnz = row_lnz(M, sr, T);
+  out.bad = row_bad(M, sr);
   return out;
 }
 
@@ -491,6 +471,8 @@ struct StreamArgs {
   int compact;
   RowPartial* part;      // [B*(P+K*G)][cpr]: slot b*P+j, then B*P + (b*K+k)*G+j
   int32_t* rank_out;     // [B + 1]: sampled batch rows before b; [B] = their total
+  uint32_t* clear;       // [nclear] per-chain counters the next launch counts on, zeroed here
+  int64_t nclear;
   // The chunk-index divisions (by cpr, P, K*G, G) as multiply-shifts: every
   // chunk index is below 2^31 (the host rejects larger calls).
   FastDiv by_cpr, by_p, by_kg, by_g;
@@ -514,6 +496,9 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
   const int nchunks = int((rs.B + 63) / 64);
   int64_t nrows = a.nrows;
   if (threadIdx.x == 0) s_claim = 0u;
+  for (int64_t i = int64_t(blockIdx.x) * kStreamBlock + threadIdx.x; i < a.nclear;
+       i += int64_t(gridDim.x) * kStreamBlock)
+    a.clear[i] = 0u;
   __syncthreads();
   if (a.compact) {
     build_sampled_table(rs.temp, rs.B, tab);
@@ -578,7 +563,10 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
       const bool sampled = T > 0.0f;
       float am = -INFINITY;
       int32_t ai = INT_MAX;
+      uint32_t nan_seen = 0;  // greedy rows: a NaN anywhere in the chunk
       if (!sampled || ARGMAX_ALL) {
+#pragma unroll
+        for (int u = 0; u < CL; ++u) nan_seen |= nan_bits<DT>(r[u]);
 #pragma unroll
         for (int u = 0; u < CL; ++u)
 #pragma unroll
@@ -627,10 +615,15 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
 #pragma unroll
           for (int off = kWave / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
           sum *= 1.0 - double(d) * 0.69314718055994530942;
+        } else {
+          // every entry -inf or NaN (fmaxf passes NaN by): carry a NaN in the sum
+#pragma unroll
+          for (int u = 0; u < CL; ++u) nan_seen |= nan_bits<DT>(r[u]);
+          if (__ballot(nan_seen != 0)) sum = NAN;
         }
         out = RowPartial{m, ai, sum};
       } else {
-        out = RowPartial{am, ai, 0.0};
+        out = RowPartial{am, ai, __ballot(nan_seen != 0) ? double(NAN) : 0.0};
       }
     }
     if (lane == 0) a.part[slot * a.cpr + (c - rho * a.cpr)] = out;
@@ -939,156 +932,6 @@ struct ChainArgs {
   FastDiv by_nsplit, by_k;
 };
 
-// The step's accept stage as its own launch, for grids too large to be
-// resident at once (then every split repeating the prologue would cost a
-// round of latency per dispatch round): one workgroup per chain merges the
-// chain's rows from the stream partials, gathers ln p / ln q at the draft
-// tokens, draws the accept uniforms and finds the first rejection by one
-// wavefront ballot. It writes the chain's outputs and the draw kernel's
-// ChainInfo.
-constexpr int kAcceptBlock = 1024;
-constexpr int kAcceptWaves = kAcceptBlock / kWave;
-constexpr int kAcceptRows = 2;  // rows per wavefront per pass
-static_assert(kAcceptWaves * kAcceptRows >= 17, "one pass covers a gamma = 8 chain");
-
-template <int DT>
-__global__ __launch_bounds__(kAcceptBlock) void accept_kernel(ChainArgs a) {
-  constexpr int esz = DT == SV_BF16 ? 2 : 4;
-  __shared__ double s_lnz[kMaxRowsPerChain];
-  __shared__ int32_t s_amax[SV_MAX_GAMMA + 1];
-  __shared__ int32_t s_rowbad[kAcceptWaves];
-  __shared__ int32_t s_n;
-  const RowSet& rs = a.rs;
-  const int64_t chain = blockIdx.x;
-  const int64_t b = fast_div(uint32_t(chain), a.by_k);
-  const int64_t k = chain - b * rs.K;
-  const int G = int(rs.G);
-  const int P = G + 1;
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
-  const float T = rs.temp[b];
-  const bool sampled = T > 0.0f;
-  const bool greedy = T == 0.0f;
-
-  {
-    // The merges of the chain's rows (target rows 0..G, then draft rows
-    // (k, 0..G-1) when sampled) go first: wavefront w merges rows w, w + W
-    // (W wavefronts), the partial loads of both rows in flight together. The
-    // draft tokens are loaded before them and the logits at the tokens after
-    // the partials arrive, so those round trips overlap the reductions.
-    const int wv = t / kWave;
-    int32_t x = 0;
-    bool tok_bad = false;
-    if (t < G) {
-      x = a.tokens[chain * G + t];
-      tok_bad = x < 0 || int64_t(x) >= a.V;
-    }
-    const int nr = P + (sampled ? G : 0);
-    int32_t row_bad = 0;
-    float zt = 0.0f, zd = 0.0f;
-    double log_u = 0.0;
-    for (int base = wv; base < nr || base == wv; base += kAcceptRows * kAcceptWaves) {
-      int64_t rho[kAcceptRows];
-#pragma unroll
-      for (int r = 0; r < kAcceptRows; ++r) {
-        const int ri = base + kAcceptWaves * r;
-        rho[r] = ri >= nr ? -1 : ri < P ? b * P + ri : rs.B * P + chain * G + (ri - P);
-      }
-      float m[kAcceptRows];
-      int32_t idx[kAcceptRows];
-      double s[kAcceptRows];
-      lane_fold<kAcceptRows>(a.part, rho, a.cpr, T, m, idx, s);
-      if (base == wv && t < G) {
-        // wavefront 0: the logits at the draft tokens and the accept uniforms
-        if (!tok_bad && sampled) {
-          zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + t * rs.tsj), x);
-          zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + t * rs.dsj), x);
-        }
-        const uint64_t pos = uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(t);
-        const Philox4 r = philox4x32_10(0u, uint32_t(pos), uint32_t(chain), kPurposeAccept,
-                                        uint32_t(a.seed), uint32_t(a.seed >> 32));
-        log_u = log_uniform_d(unit_uniform_d(r.w[0]));
-      }
-      // rows one at a time through a shifting window (rolled: less code)
-#pragma unroll 1
-      for (int r = 0; r < kAcceptRows; ++r) {
-        const int ri = base + kAcceptWaves * r;
-        if (ri < nr) {  // uniform across the wavefront
-          const RowStat st = wave_reduce_row(m[0], idx[0], s[0], T);
-          if (lane == 0) {
-            s_lnz[ri] = st.lnz;
-            if (!(st.m > -INFINITY)) row_bad = SV_ERR_ROW;
-            if (ri < P) {
-              s_amax[ri] = st.idx == INT_MAX ? 0 : st.idx;
-              if (k == 0 && a.lnz_t_out) a.lnz_t_out[b * P + ri] = st.lnz;
-            } else if (a.lnz_d_out) {
-              a.lnz_d_out[chain * G + (ri - P)] = st.lnz;
-            }
-          }
-        }
-#pragma unroll
-        for (int q = 0; q + 1 < kAcceptRows; ++q) {
-          m[q] = m[q + 1];
-          idx[q] = idx[q + 1];
-          s[q] = s[q + 1];
-        }
-      }
-    }
-    if (lane == 0) s_rowbad[wv] = row_bad;
-    __syncthreads();
-    // accept tests of the G positions in wavefront 0, first rejection by ballot
-    if (t < kWave) {
-      bool acc = false;
-      if (t < G) {
-        const int j = t;
-        double lp = 0.0, lq = 0.0;
-        if (!tok_bad) {
-          if (sampled) {
-            lp = double(zt) / double(T) - s_lnz[j];
-            lq = double(zd) / double(T) - s_lnz[P + j];
-            acc = log_u < lp - lq;
-          } else if (greedy) {
-            acc = x == s_amax[j];
-            lp = acc ? 0.0 : -INFINITY;
-            lq = 0.0;
-          }
-        }
-        if (a.logp) a.logp[chain * G + j] = float(lp);
-        if (a.logq) a.logq[chain * G + j] = float(lq);
-      }
-      const uint64_t acc_mask = __ballot(acc);
-      const uint64_t bad_mask = __ballot(tok_bad);
-      if (t == 0) {
-        const int n = __builtin_ctzll(~acc_mask);  // leading accepts (<= G: bit G of ~mask is set)
-        int32_t err = 0;
-        for (int w = 0; w < kAcceptWaves; ++w) err |= s_rowbad[w];
-        if (bad_mask) err |= SV_ERR_TOKEN;
-        if (!(sampled || greedy)) err |= SV_ERR_TEMP;
-        s_n = err ? -1 : n;
-        if (err) {
-          a.accept_len[chain] = -1;
-          a.out_token[chain] = -1;
-          if (a.dev_err) atomicOr(a.dev_err, err);
-        } else {
-          a.accept_len[chain] = n;
-          if (greedy) a.out_token[chain] = s_amax[n];
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  if (t == 0) {
-    const int n = s_n;
-    ChainInfo ci;
-    ci.n = (n >= 0 && sampled) ? n : -1;
-    ci.lzt = n >= 0 ? s_lnz[n] : 0.0;
-    ci.lzd = (n >= 0 && n < G && sampled) ? s_lnz[P + n] : 0.0;
-    ci.pad[0] = ci.pad[1] = ci.pad[2] = 0;
-    a.info[chain] = ci;
-  }
-}
-
 // specverify_residual_sample: one thread per chain turns the given n and
 // normalisers into the draw kernel's ChainInfo (greedy rows: the token is the
 // target row's argmax at n).
@@ -1101,6 +944,7 @@ __global__ __launch_bounds__(kBlock) void given_kernel(ChainArgs a, int64_t chai
   const int P = G + 1;
   const float T = rs.temp[b];
   const bool sampled = T > 0.0f;
+  if (a.cnt) a.cnt[chain] = 0u;  // the draw launch counts this chain's splits from zero
   const int32_t n0 = a.n_in[chain];
   const int n = (n0 < 0 || n0 > G) ? -1 : n0;
   if (T == 0.0f && n >= 0) a.out_token[chain] = a.amax_in[b * P + n];
@@ -1184,17 +1028,13 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
       const int32_t oi = __shfl_xor(I, off, kWave);
       better_max(M, I, om, oi);
     }
-    double sr = 0.0;
-    if (sampled && M > -INFINITY) sr = m > -INFINITY ? s * exp2_scale((double(m) - double(M)) * k2) : 0.0;
+    double sr = (sampled && M > -INFINITY && m > -INFINITY) ? s * exp2_scale((double(m) - double(M)) * k2) : s;
 #pragma unroll
     for (int off = kRowLanes / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
     if (has && gl == 0) {
-      double lnz;
-      if (sampled) lnz = M > -INFINITY ? double(M) / double(T) + log(sr) : double(M);
-      else if (greedy) lnz = double(M);
-      else lnz = NAN;
+      const double lnz = row_lnz(M, sr, T);
       s_lnz[ri] = lnz;
-      if (!(M > -INFINITY)) bad = SV_ERR_ROW;
+      if (row_bad(M, sr)) bad = SV_ERR_ROW;
       if (ri < P) {
         s_amax[ri] = I == INT_MAX ? 0 : I;
         if (lead && k == 0 && a.lnz_t_out) a.lnz_t_out[b * P + ri] = lnz;
@@ -1253,6 +1093,20 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
     }
   }
   __syncthreads();
+}
+
+// The step's accept stage as its own launch, for grids too large to be
+// resident at once (then every split repeating the prologue would cost a
+// round of latency per dispatch round): one workgroup per chain runs the
+// draws' prologue once (the same fold order, so the same ln Z bits) and
+// leaves n and the normalisers in ChainInfo for the draw kernel.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void accept_kernel(ChainArgs a) {
+  __shared__ double s_lnz[kMaxRowsPerChain];
+  __shared__ int32_t s_amax[SV_MAX_GAMMA + 1];
+  __shared__ int32_t s_rowbad[kRowsPerPass];
+  __shared__ int32_t s_n;
+  chain_prologue<DT>(a, blockIdx.x, true, s_lnz, s_amax, s_rowbad, &s_n);
 }
 
 // One workgroup per (chain, split of kSplit ids). FUSED (the step): the
@@ -1327,7 +1181,6 @@ void draw_kernel(ChainArgs a) {
         stores_done();
         const uint32_t prev = bump32(a.cnt + chain);
         s_last = prev == uint32_t(a.nsplit - 1);
-        if (s_last) pub32(a.cnt + chain, 0u);  // every split is counted: zero for the next call
       }
     }
   }
@@ -2081,9 +1934,11 @@ struct Layout {
   size_t off_part, off_rank, off_info, off_top, total;
 };
 
-// Chain counters at the start of every workspace, at a fixed place whatever
-// the sizes: zero before a workspace's first use, and every completed call
-// leaves them zero. Steps with more chains pick their tokens in finish_kernel.
+// Chain counters at the start of every workspace. The first launch of every
+// call that counts on them zeroes the ones it uses (the stream kernel, or
+// given_kernel), so a workspace needs no preparation and an interrupted call
+// leaves nothing behind. Steps with more chains pick their tokens in
+// finish_kernel.
 constexpr int64_t kMaxCountedChains = 65536;
 constexpr size_t kCounterBytes = kMaxCountedChains * sizeof(uint32_t);
 
@@ -2221,7 +2076,7 @@ void launch_chain_finish(const ChainArgs& ca, bool given, hipStream_t st) {
     hipLaunchKernelGGL((draw_kernel<DT, VEC, true>), grid, dim3(kBlock), 0, st, ca);
   } else {
     // more workgroups than fit at once: n per chain in its own launch
-    hipLaunchKernelGGL((accept_kernel<DT>), dim3(unsigned(chains)), dim3(kAcceptBlock), 0, st, ca);
+    hipLaunchKernelGGL((accept_kernel<DT>), dim3(unsigned(chains)), dim3(kBlock), 0, st, ca);
     hipLaunchKernelGGL((draw_kernel<DT, VEC, false>), grid, dim3(kBlock), 0, st, ca);
   }
   if (ca.cnt) return;  // the chains' last splits picked the tokens
@@ -2342,6 +2197,19 @@ void launch_topf(bool wide, dim3 grid, hipStream_t st, const TopFArgs& ta) {
     hipLaunchKernelGGL((topf_kernel<DT, VEC, kTopFSample>), grid, dim3(kTopFBlock), 0, st, ta);
 }
 
+int step_checks(const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* draft_tokens, int64_t B, int64_t K, int64_t gamma, int64_t V,
+                int64_t t_stride_b, int64_t t_stride_j, int64_t d_stride_b, int64_t d_stride_k,
+                int64_t d_stride_j, const float* temperature, const int32_t* accept_len,
+                const int32_t* out_token);
+int step_launch(const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* draft_tokens, int64_t B, int64_t K, int64_t gamma, int64_t V,
+                int64_t t_stride_b, int64_t t_stride_j, int64_t d_stride_b, int64_t d_stride_k,
+                int64_t d_stride_j, const float* temperature, uint64_t seed, const int64_t* pos0,
+                int32_t* accept_len, int32_t* out_token, float* logp, float* logq,
+                double* lnZ_target, double* lnZ_draft, int32_t* device_error, void* workspace,
+                hipStream_t st);
+
 }  // namespace
 
 extern "C" {
@@ -2455,6 +2323,27 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
                     float* logp, float* logq, double* lnZ_target, double* lnZ_draft,
                     int32_t* device_error, void* workspace, size_t workspace_bytes,
                     void* stream) {
+  int status = step_checks(target_logits, draft_logits, dtype, draft_tokens, B, K, gamma, V,
+                           t_stride_b, t_stride_j, d_stride_b, d_stride_k, d_stride_j,
+                           temperature, accept_len, out_token);
+  if (status != SV_OK) return status;
+  const Layout L = step_layout(B, K, gamma, V, dtype);
+  if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
+  return step_launch(target_logits, draft_logits, dtype, draft_tokens, B, K, gamma, V,
+                     t_stride_b, t_stride_j, d_stride_b, d_stride_k, d_stride_j, temperature,
+                     seed, pos0, accept_len, out_token, logp, logq, lnZ_target, lnZ_draft,
+                     device_error, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+int step_checks(const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* draft_tokens, int64_t B, int64_t K, int64_t gamma, int64_t V,
+                int64_t t_stride_b, int64_t t_stride_j, int64_t d_stride_b, int64_t d_stride_k,
+                int64_t d_stride_j, const float* temperature, const int32_t* accept_len,
+                const int32_t* out_token) {
   if (!target_logits || !draft_logits || !draft_tokens || !temperature || !accept_len ||
       !out_token)
     return SV_EINVAL;
@@ -2462,17 +2351,26 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
   if (t_stride_b < 0 || t_stride_j < 0 || d_stride_b < 0 || d_stride_k < 0 || d_stride_j < 0)
     return SV_EINVAL;
   if (check_dtype(dtype) != SV_OK) return SV_EDTYPE;
+  if (!stream_chunks_ok(step_layout(B, K, gamma, V, dtype))) return SV_EINVAL;
+  return SV_OK;
+}
+
+// The step's launches on stream st with a workspace already checked for size
+// and alignment.
+int step_launch(const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* draft_tokens, int64_t B, int64_t K, int64_t gamma, int64_t V,
+                int64_t t_stride_b, int64_t t_stride_j, int64_t d_stride_b, int64_t d_stride_k,
+                int64_t d_stride_j, const float* temperature, uint64_t seed, const int64_t* pos0,
+                int32_t* accept_len, int32_t* out_token, float* logp, float* logq,
+                double* lnZ_target, double* lnZ_draft, int32_t* device_error, void* workspace,
+                hipStream_t st) {
   const Layout L = step_layout(B, K, gamma, V, dtype);
-  if (!stream_chunks_ok(L)) return SV_EINVAL;
-  int status = SV_OK;
-  if (!workspace_ok(workspace, workspace_bytes, L.total, &status)) return status;
   const int esz = esize(dtype);
   const bool vec = logits_vec_ok(target_logits, draft_logits, esz, t_stride_b, t_stride_j,
                                  d_stride_b, d_stride_k, d_stride_j);
   auto* base = reinterpret_cast<char*>(workspace);
   auto* part = reinterpret_cast<RowPartial*>(base + L.off_part);
   auto* rank = reinterpret_cast<int32_t*>(base + L.off_rank);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const RowSet rs{target_logits, t_stride_b, t_stride_j, draft_logits, d_stride_b, d_stride_k,
                   d_stride_j, B, gamma + 1, K, gamma, temperature};
   const int compact = B <= kMaxCompactB ? 1 : 0;
@@ -2486,6 +2384,8 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
   sa.compact = compact;
   sa.part = part;
   sa.rank_out = compact ? rank : nullptr;
+  sa.clear = B * K <= kMaxCountedChains ? reinterpret_cast<uint32_t*>(base) : nullptr;
+  sa.nclear = sa.clear ? B * K : 0;
   launch_stream(dtype, vec, false, sa, st);
 
   ChainArgs ca{};
@@ -2510,6 +2410,10 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
   launch_chain(dtype, vec, ca, false, st);
   return launch_status();
 }
+
+}  // namespace
+
+extern "C" {
 
 const char* specverify_status_string(int status) {
   switch (status) {

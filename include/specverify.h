@@ -42,11 +42,10 @@
  * - Results are bit-deterministic: reductions merge in a fixed order and no
  *   floating-point atomics are used.
  * - `workspace` is device scratch of at least specverify_workspace_size()
- *   bytes, 256-byte aligned, which the caller zero-fills once before its
- *   first use. Its first bytes hold per-chain counters through which the
- *   sampling workgroups of one launch find the last of a chain's splits;
- *   every call that completes leaves them zero and nothing else writes them,
- *   so one buffer serves any number of calls of any sizes (within its size)
+ *   bytes, 256-byte aligned, with any contents: each call's first launch
+ *   clears what must start at zero (the per-chain counters through which the
+ *   sampling workgroups of one launch find the last of a chain's splits), so
+ *   one buffer serves any number of calls of any sizes (within its size)
  *   ordered on one stream. Calls that overlap in time on one buffer race.
  */
 #ifndef SPECVERIFY_H
@@ -75,8 +74,9 @@ extern "C" {
  * out_token are set to -1 when any of them applies to it. */
 #define SV_ERR_TOKEN 1     /* a draft token outside [0, V)                   */
 #define SV_ERR_TEMP 2      /* temperature negative or NaN                    */
-#define SV_ERR_ROW 4       /* a needed row whose largest logit is -inf (all
-                              entries masked) or NaN                         */
+#define SV_ERR_ROW 4       /* a needed row whose largest logit is not
+                              finite: every entry -inf (all masked), or any
+                              +inf or NaN entry                              */
 
 /* Size limits checked on the host. */
 #define SV_MAX_GAMMA 32
@@ -103,9 +103,11 @@ size_t specverify_workspace_size(int64_t B, int64_t K, int64_t gamma, int64_t V,
  *   temperature  [B] float
  *   lnZ          [B, P] double out: ln sum_v exp(z_v / T_b) for T_b > 0;
  *                max_v z_v for T_b == 0 (the T -> 0 limit of T * ln Z);
- *                NaN for T_b < 0 or NaN. An all -inf row gives -inf.
+ *                NaN for T_b < 0 or NaN. An all -inf row gives -inf; a row
+ *                holding a NaN gives NaN, and so does a +inf entry when
+ *                T_b > 0 (for T_b == 0 the maximum is +inf).
  *   argmax       [B, P] int32 out, or NULL: lowest id of the row maximum of
- *                the raw logits, for every row.
+ *                the raw logits, for every row (NaN entries are passed by).
  * Status: SV_EINVAL (null logits/temperature/lnZ, B/P/V < 1, V >= 2^31,
  * negative stride, or rows of 2^31 or more 8 KB chunks: over 16 TiB of
  * logits), SV_EDTYPE, SV_EWORKSPACE, SV_EALIGN, SV_EHIP.

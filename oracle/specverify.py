@@ -74,7 +74,8 @@ def scaled_logits(z: np.ndarray, T) -> np.ndarray:
 def log_normalizer(s: np.ndarray) -> np.ndarray:
     """ln sum_v exp(s_v) over the last axis with the row maximum factored out.
 
-    A row that is entirely -inf gives -inf; a NaN or +inf maximum passes through.
+    A row that is entirely -inf gives -inf. A row holding a NaN or a +inf has no
+    normaliser (ln p of its +inf entry would be inf - inf): NaN.
     """
     m = np.max(s, axis=-1)
     finite = np.isfinite(m)
@@ -82,7 +83,7 @@ def log_normalizer(s: np.ndarray) -> np.ndarray:
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         total = np.sum(np.exp(s - m0[..., None]), axis=-1)
         out = m0 + np.log(total)
-    return np.where(finite, out, m)
+    return np.where(finite, out, np.where(np.isneginf(m), m, np.nan))
 
 
 def normalize_rows(z: np.ndarray, T) -> tuple[np.ndarray, np.ndarray]:

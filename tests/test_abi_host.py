@@ -207,3 +207,4 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(sv.SpecVerifyError):
         sv.specverify_normalize(torch.zeros(1, 2, 8), torch.ones(1))
+

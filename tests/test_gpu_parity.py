@@ -13,7 +13,7 @@ import torch
 import device_draft_verification_specverify_amd as sv
 import oracle
 import workloads
-from gpu_helpers import compare_step, device, logits_to_dev, step_on_gpu, to_dev
+from gpu_helpers import LNZ_TOL, compare_step, device, logits_to_dev, step_on_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -251,7 +251,7 @@ def test_workspace_reused_across_shapes_and_calls():
     ws_bytes = max(sv.workspace_size(s["B"], s.get("K", 1), s.get("gamma", 8), s["V"],
                                      sv.SV_BF16 if s["dtype"] == "bf16" else sv.SV_F32)
                    for s in shapes)
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=device())
+    ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device=device())  # any contents
     for i, s in enumerate(shapes):
         print(f"[case] shared workspace call {i}: {s}", flush=True)
         w = workloads.make("c3", seed=i, temps=("choice", (0.0, 0.3, 1.0)), **s)
@@ -292,18 +292,26 @@ def test_bandit_loop_over_draft_models_on_the_gpu():
         zd = zt[:, None, :-1] + rng.normal(0, sigma, size=base.draft.shape)
         models.append(logits_to_dev(synth._store(zd, "bf16"), "bf16"))
     bandit = sv.Bandit(3, sv.BANDIT_UCB1)
-    picks = []
+    picks, rewards = [], []
     for step in range(60):
         arm = bandit.select()
         draft = models[arm]
         # draft tokens: the draft model's own argmax, so every arm proposes its best guess
         toks = draft.float().argmax(dim=-1).to(torch.int32).contiguous()
         out = sv.specverify_step(target, draft, toks, temp, 1000 + step, to_dev(base.pos0))
-        bandit.update(arm, sv.step_reward(out.accept_len, base.gamma))
+        reward = sv.step_reward(out.accept_len, base.gamma)
+        bandit.update(arm, reward)
         picks.append(arm)
+        rewards.append(reward)
     counts = np.bincount(picks, minlength=3)
     print(f"[parity] bandit picks {counts.tolist()}", flush=True)
     assert counts[0] > counts[1] and counts[0] > counts[2]
+    # the oracle's selector, fed the same rewards, picks the same arm at every step
+    from oracle import bandit as bd
+    ora = bd.Bandit(3, bd.UCB1)
+    for step, (arm, reward) in enumerate(zip(picks, rewards)):
+        assert ora.select() == arm, step
+        ora.update(arm, reward)
 
 
 def test_branch_prune_matches_the_oracle():
@@ -321,3 +329,78 @@ def test_branch_prune_matches_the_oracle():
         assert np.array_equal(conf.cpu().numpy(), c_ref)
         assert np.array_equal(plen.cpu().numpy(), l_ref)
         assert np.array_equal(mask.cpu().numpy().astype(bool), m_ref)
+
+
+def test_non_finite_rows_set_the_row_error():
+    # Reading of the input-error rule: a needed row whose largest logit is not finite (all
+    # -inf, or any +inf or NaN entry) poisons its chains; a greedy row's draft rows are
+    # never read, so a NaN there is no error.
+    w = workloads.make("c3", B=7, V=9000, temps=("const", 0.7))
+    w.temperature[2] = 0.0
+    w.temperature[5] = 0.0
+    nan, inf = (0x7FC0, 0x7F80) if w.dtype == "bf16" else (np.float32(np.nan), np.float32(np.inf))
+    w.target[1, 2, 17] = nan               # one NaN among finite logits
+    w.target[2, 1, 4000] = nan             # greedy row: NaN in the target row
+    w.draft[3, 0, 1, 8191] = inf           # +inf in a draft row
+    w.target[4, 0, :4096] = nan            # a whole chunk of NaN (its maximum reads -inf)
+    w.draft[5, 0, 0, 5] = nan              # greedy batch row: draft logits are not needed
+    w.target[6, 8, 100] = inf              # +inf in the bonus row
+    print("[case] non-finite rows", flush=True)
+    gpu = step_on_gpu(w)
+    ref = _ref(w)
+    assert ref["error"] == 4 and int(gpu["device_error"][0]) == 4
+    assert np.array_equal(gpu["accept_len"], ref["accept_len"])
+    for b in (1, 2, 3, 4, 6):
+        assert gpu["accept_len"][b, 0] == -1 and gpu["out_token"][b, 0] == -1, b
+    good = np.array([0, 5])
+    compare_step({k: (v[good] if k not in ("device_error",) and v is not None else v)
+                  for k, v in gpu.items()},
+                 {k: (v[good] if isinstance(v, np.ndarray) and v.ndim >= 1 else v)
+                  for k, v in ref.items()}, w.temperature[good])
+    # the normalise entry point on the same rows: NaN where the oracle has no normaliser
+    t = logits_to_dev(w.target, w.dtype)
+    lnz, _ = sv.specverify_normalize(t, to_dev(w.temperature), want_argmax=True)
+    torch.cuda.synchronize()
+    rl, _ = oracle.normalize_rows(oracle.decode_logits(w.target, w.dtype), w.temperature[:, None])
+    lnz = lnz.cpu().numpy()
+    assert np.array_equal(np.isnan(lnz), np.isnan(rl))
+    assert np.array_equal(np.isinf(lnz), np.isinf(rl))
+    fin = np.isfinite(rl)
+    assert np.all(np.abs(lnz[fin] - rl[fin]) <= LNZ_TOL)
+
+
+def test_empty_residual_support_draws_from_p_unmasked():
+    # Draft bytes equal to target bytes: ln q - ln p is exactly 0 for every id on both
+    # sides, so the residual support is empty with no rounding ambiguity and the token is
+    # the draw from p_n with the same noise. The oracle flags every such chain (an id
+    # within eps of the support boundary), so this compares them unmasked; only chains
+    # whose p_n draw has its runner-up within 2e-6 are left out, and they are counted.
+    for V, dt in ((20000, "bf16"), (3001, "f32")):
+        print(f"[case] empty support V={V} {dt}", flush=True)
+        w = workloads.make("c3", B=16, V=V, gamma=4, dtype=dt, temps=("choice", (0.4, 1.0)))
+        w.draft[:, 0] = w.target[:, :4]
+        zt = oracle.decode_logits(w.target, w.dtype)
+        zd = oracle.decode_logits(w.draft, w.dtype)
+        T = w.temperature.astype(np.float64)
+        lnz_t, am = oracle.normalize_rows(zt, T[:, None])
+        lnz_d = lnz_t[:, None, :4].copy()
+        n = np.random.default_rng(V).integers(0, 4, size=(w.B, 1))
+        tok, _, empty = oracle.specverify.sample_tokens(zt, zd, T, lnz_t, lnz_d, am, n, w.seed,
+                                                       w.pos0, np.arange(w.B)[:, None])
+        assert empty.all()
+        out = sv.specverify_residual_sample(
+            logits_to_dev(w.target, w.dtype), logits_to_dev(w.draft, w.dtype), to_dev(w.temperature),
+            to_dev(lnz_t), to_dev(lnz_d), to_dev(am.astype(np.int32)), to_dev(n.astype(np.int32)),
+            w.seed, to_dev(w.pos0))
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        robust = np.ones(w.B, dtype=bool)
+        for b in range(w.B):
+            lp = zt[b, n[b, 0]] / T[b] - lnz_t[b, n[b, 0]]
+            G = oracle.specverify.sampling_noise(w.seed, np.array([b]), w.pos0[b:b + 1] + n[b],
+                                                 w.V)[0]
+            sc = np.sort(lp + G)
+            robust[b] = sc[-1] - sc[-2] >= 2e-6
+        print(f"[parity] empty support: {int(robust.sum())} of {w.B} compared", flush=True)
+        assert robust.sum() >= w.B - 1
+        assert np.array_equal(got[robust, 0], tok[robust, 0]), (got.ravel(), tok.ravel())

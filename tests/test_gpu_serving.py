@@ -49,7 +49,8 @@ def test_one_workspace_serves_every_entry_point():
                sv.workspace_size(w.B, 0, 2 * w.gamma, w.V, sv.SV_BF16),
                int(sv.load_library().specverify_accept_prob_workspace_size(w.B, w.K, w.gamma,
                                                                              w.V, sv.SV_BF16)))
-    shared = torch.zeros(need, dtype=torch.uint8, device=dev)
+    # any contents: each call's first launch clears the counters it counts on
+    shared = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
     ref1 = _host(sv.StepPlan(t, d, tok, temp, w.seed, pos0)())
     ref2 = _host(sv.StepPlan(t2, d2, tok2, temp2, w2.seed, pos02)())
     p1 = sv.StepPlan(t, d, tok, temp, w.seed, pos0, ws=shared)
@@ -64,7 +65,6 @@ def test_one_workspace_serves_every_entry_point():
         _same(_host(p1()), ref1)
         _same(_host(p2()), ref2)
     torch.cuda.synchronize(dev)
-    assert int(shared[:4 * 64].count_nonzero().item()) == 0   # counters of these chains left zero
 
 
 def test_two_batches_on_two_streams():
