@@ -19,6 +19,8 @@ LIBRARY = os.path.join(HERE, "libspecverify.so")
 SV_F32 = 0
 SV_BF16 = 1
 SV_OK = 0
+SV_ESCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 32 << 20
 SV_ERR_TOKEN = 1
 SV_ERR_TEMP = 2
 SV_ERR_ROW = 4
@@ -43,6 +45,8 @@ _SIGNATURES = {
                                           _P]),
     "specverify_step": (_INT, [_P, _P, _INT, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                _I64, _P, _U64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "specverify_step_noalloc": (_INT, [_P, _P, _INT, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                       _I64, _I64, _P, _U64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "specverify_accept_prob_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
     "specverify_accept_prob": (_INT, [_P, _P, _INT, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                       _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -218,7 +222,8 @@ class StepPlan:
 
     def __init__(self, target, draft, tokens, temperature, seed: int, pos0=None, *,
                  want_logprobs: bool = True, want_normalizers: bool = True,
-                 want_error: bool = True, ws: torch.Tensor | None = None):
+                 want_error: bool = True, ws: torch.Tensor | None = None,
+                 noalloc: bool = False):
         self.lib = load_library()
         _logits(target, 3, "target")
         _logits(draft, 4, "draft")
@@ -254,9 +259,14 @@ class StepPlan:
             temperature.data_ptr(), self.seed, _ptr(pos0), o.accept_len.data_ptr(),
             o.out_token.data_ptr(), _ptr(o.logp), _ptr(o.logq), _ptr(o.lnZ_target),
             _ptr(o.lnZ_draft), _ptr(o.device_error))
-        self.ws = ws if ws is not None else workspace(B, K, g, V, self.dtype, dev)
-        self._args += (self.ws.data_ptr(), self.ws.numel())
-        self._fn, self._name = self.lib.specverify_step, "specverify_step"
+        if noalloc:
+            # the library's own scratch (specverify_step_noalloc): no workspace here
+            self.ws = None
+            self._fn, self._name = self.lib.specverify_step_noalloc, "specverify_step_noalloc"
+        else:
+            self.ws = ws if ws is not None else workspace(B, K, g, V, self.dtype, dev)
+            self._args += (self.ws.data_ptr(), self.ws.numel())
+            self._fn, self._name = self.lib.specverify_step, "specverify_step"
         self.device = dev
 
     def __call__(self, stream: int | None = None) -> StepOutputs:

@@ -43,6 +43,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "specverify.h"
 
@@ -2212,6 +2213,38 @@ int step_launch(const void* target_logits, const void* draft_logits, int dtype,
 
 }  // namespace
 
+// Scratch of specverify_step_noalloc, for callers that cannot allocate: one
+// copy per GPU, resident from the library's load on that GPU until the process
+// ends. Host code never passes the array's name to a kernel (on the host it is
+// only a stand-in for the symbol): scratch_address() looks up each device's
+// own address once, with that device current, and every launch uses that.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+int scratch_address(void** out) {
+  static std::atomic<void*> cache[kMaxDevices];
+  static std::mutex lock;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_EHIP;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> hold(lock);
+    p = cache[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+        return SV_EHIP;
+      cache[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t specverify_workspace_size(int64_t B, int64_t K, int64_t gamma, int64_t V, int dtype) {
@@ -2335,6 +2368,28 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
                      device_error, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
+int specverify_step_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                            const int32_t* draft_tokens, int64_t B, int64_t K, int64_t gamma,
+                            int64_t V, int64_t t_stride_b, int64_t t_stride_j, int64_t d_stride_b,
+                            int64_t d_stride_k, int64_t d_stride_j, const float* temperature,
+                            uint64_t seed, const int64_t* pos0, int32_t* accept_len,
+                            int32_t* out_token, float* logp, float* logq, double* lnZ_target,
+                            double* lnZ_draft, int32_t* device_error, void* stream) {
+  int status = step_checks(target_logits, draft_logits, dtype, draft_tokens, B, K, gamma, V,
+                           t_stride_b, t_stride_j, d_stride_b, d_stride_k, d_stride_j,
+                           temperature, accept_len, out_token);
+  if (status != SV_OK) return status;
+  if (step_layout(B, K, gamma, V, dtype).total > size_t(SV_NOALLOC_SCRATCH_BYTES))
+    return SV_ESCRATCH;
+  void* ws = nullptr;
+  status = scratch_address(&ws);
+  if (status != SV_OK) return status;
+  return step_launch(target_logits, draft_logits, dtype, draft_tokens, B, K, gamma, V,
+                     t_stride_b, t_stride_j, d_stride_b, d_stride_k, d_stride_j, temperature,
+                     seed, pos0, accept_len, out_token, logp, logq, lnZ_target, lnZ_draft,
+                     device_error, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"
 
 namespace {
@@ -2423,6 +2478,9 @@ const char* specverify_status_string(int status) {
     case SV_EWORKSPACE: return "workspace missing or too small";
     case SV_EALIGN: return "workspace not 256-byte aligned";
     case SV_EHIP: return "HIP kernel launch failed";
+    case SV_ESCRATCH:
+      return "sizes need more scratch than specverify_step_noalloc holds "
+             "(SV_NOALLOC_SCRATCH_BYTES); use specverify_step with a workspace";
     default: return "unknown status";
   }
 }

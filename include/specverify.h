@@ -69,6 +69,11 @@ extern "C" {
 #define SV_EWORKSPACE (-3) /* workspace missing or smaller than required     */
 #define SV_EALIGN (-4)     /* workspace not 256-byte aligned                 */
 #define SV_EHIP (-5)       /* a kernel launch failed                         */
+#define SV_ESCRATCH (-6)   /* specverify_step_noalloc: sizes need more scratch
+                              than SV_NOALLOC_SCRATCH_BYTES                  */
+
+/* Device scratch held by specverify_step_noalloc on every GPU it runs on. */
+#define SV_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Bits OR-ed into the optional device error word; the chain's accept_len and
  * out_token are set to -1 when any of them applies to it. */
@@ -197,6 +202,28 @@ int specverify_step(const void* target_logits, const void* draft_logits, int dty
                     int32_t* accept_len, int32_t* out_token, float* logp, float* logq,
                     double* lnZ_target, double* lnZ_draft, int32_t* device_error,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * specverify_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, outputs and results as specverify_step without the
+ * workspace: the step runs in a scratch array that the library holds on each
+ * GPU from its load until the process ends (SV_NOALLOC_SCRATCH_BYTES, 32 MiB;
+ * enough for B = 512 rows x K = 4 branches at gamma = 8, V = 128256). The call
+ * allocates nothing and leaves no state that the next call needs: the step's
+ * first launch clears what must start at zero. Every call on one GPU shares
+ * that GPU's scratch, so calls that overlap in time on one GPU (on different
+ * streams, or from different threads) race; order them on one stream.
+ * Status: as specverify_step, plus SV_ESCRATCH when specverify_workspace_size
+ * for these sizes exceeds SV_NOALLOC_SCRATCH_BYTES (nothing is enqueued).
+ */
+int specverify_step_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                            const int32_t* draft_tokens, int64_t B, int64_t K, int64_t gamma,
+                            int64_t V, int64_t t_stride_b, int64_t t_stride_j, int64_t d_stride_b,
+                            int64_t d_stride_k, int64_t d_stride_j, const float* temperature,
+                            uint64_t seed, const int64_t* pos0, int32_t* accept_len,
+                            int32_t* out_token, float* logp, float* logq, double* lnZ_target,
+                            double* lnZ_draft, int32_t* device_error, void* stream);
 
 /*
  * Bytes of workspace that specverify_accept_prob needs for these sizes. Its

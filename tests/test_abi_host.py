@@ -27,6 +27,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"specverify_workspace_size", "specverify_normalize", "specverify_accept",
                           "specverify_residual_sample", "specverify_step",
+                          "specverify_step_noalloc",
                           "specverify_accept_prob_workspace_size", "specverify_accept_prob",
                           "specverify_geometric_fanout", "specverify_residual_topf",
                           "specverify_cache_lookup",
@@ -208,3 +209,19 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(sv.SpecVerifyError):
         sv.specverify_normalize(torch.zeros(1, 2, 8), torch.ones(1))
 
+
+def test_noalloc_step_refuses_sizes_beyond_its_scratch_on_the_host():
+    # the size check comes before any device call: the pointers are never touched
+    lib = sv.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    B, K, g, V = 2048, 4, 8, 128256
+    assert sv.workspace_size(B, K, g, V, sv.SV_BF16) > sv.NOALLOC_SCRATCH_BYTES
+    st = lib.specverify_step_noalloc(fake, fake, sv.SV_BF16, fake, B, K, g, V, (g + 1) * V, V,
+                                     K * g * V, g * V, V, fake, 1, None, fake, fake, None, None,
+                                     None, None, None, None)
+    assert st == sv.SV_ESCRATCH
+    assert b"SV_NOALLOC_SCRATCH_BYTES" in lib.specverify_status_string(st)
+    # argument errors are reported first, as by specverify_step
+    assert lib.specverify_step_noalloc(None, fake, sv.SV_BF16, fake, B, K, g, V, 0, 0, 0, 0, 0,
+                                       fake, 1, None, fake, fake, None, None, None, None, None,
+                                       None) == -1  # SV_EINVAL
