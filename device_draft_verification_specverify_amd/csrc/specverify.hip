@@ -789,6 +789,42 @@ __device__ __forceinline__ void score_vec(const RawVec<DT>& rt, const RawVec<DT>
   }
 }
 
+// score_vec with an exact filter. -ln u >= 1 - u and w_v <= p_v give
+// key_v >= (1 - u_v) / (ln 2 * p_v); an id is skipped only when that bound,
+// less a relative 1e-5 that covers the float rounding of both sides (a few
+// units in the last place), still exceeds thr, a key that two candidates of
+// one lane already beat, so it cannot enter the wave's best two. The log, the
+// draft term, the reciprocal and the insertion run only for ids some lane of
+// the wave keeps; a kept id's key is computed exactly as in score_vec.
+template <int DT, bool RESIDUAL>
+__device__ __forceinline__ void score_vec_filtered(const RawVec<DT>& rt, const RawVec<DT>& rd,
+                                                   int64_t vi, const DrawParams& dp, float thr,
+                                                   Top2& best) {
+  const uint32_t c0 = uint32_t(vi * 2);
+  const Philox4 lo = philox4x32_10(c0, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
+  const Philox4 hi = philox4x32_10(c0 + 1u, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
+  const float bound = thr * (0.69314718f * (1.0f + 1e-5f));
+#pragma unroll
+  for (int t = 0; t < kVec; ++t) {
+    const float zt = vec_elem<DT>(rt, t);
+    const float a2 = fmaf(zt, dp.k2, -dp.L2t);
+    const float p = __builtin_amdgcn_exp2f(a2);
+    const uint32_t word = t < 4 ? lo.w[t] : hi.w[t - 4];
+    const float u = unit_uniform(word);
+    const bool keep = !(1.0f - u > bound * p);
+    if (__ballot(keep)) {
+      if (keep) {
+        const float zd = RESIDUAL ? vec_elem<DT>(rd, t) : 0.0f;
+        float w = p;
+        if constexpr (RESIDUAL) w -= __builtin_amdgcn_exp2f(a2 + fmaf(zd - zt, dp.k2, dp.D2));
+        const float e2 = -__builtin_amdgcn_logf(u);
+        const float key = w > 0.0f ? e2 * __builtin_amdgcn_rcpf(w) : INFINITY;
+        top2_push(best, key, int32_t(vi * kVec + t), zt, zd);
+      }
+    }
+  }
+}
+
 // float64 score of candidate v with target / draft logits zt, zd:
 // ln w_v + G_v with G_v = -ln(-ln u_v).
 __device__ __forceinline__ double rescore(bool residual, int32_t v, float zt, float zd, double T, double lzt,
@@ -835,8 +871,12 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
 // 8, else all but the row's last), the loads are issued unconditionally (lanes
 // past the row load the row's last vector and never score it) and the scoring
 // is unrolled, so vector it waits only for its own loads and the arithmetic of
-// the first vectors overlaps the arrival of the later ones.
-template <int DT, bool VEC, bool RESIDUAL>
+// the first vectors overlaps the arrival of the later ones. FILTER: after each
+// vector the wavefront's smallest second-best key bounds the ids worth scoring
+// (score_vec_filtered); it pays where the draws are bound by arithmetic (grids
+// of several rounds) and costs latency where a single round of workgroups is
+// bound by its dependent steps.
+template <int DT, bool VEC, bool RESIDUAL, bool FILTER>
 __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d, int64_t split,
                                            int64_t V, const DrawParams& dp) {
   const int64_t vpr = (V + kVec - 1) / kVec;
@@ -853,10 +893,24 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
       if constexpr (RESIDUAL) wd[it] = load_vec<DT, true>(row_d, vc);
     }
     Top2 best = top2_empty();
+    if constexpr (FILTER) {
+      float thr = INFINITY;  // two keys of one lane are at most thr
 #pragma unroll
-    for (int it = 0; it < kSampleIters; ++it) {
-      const int64_t vi = vi0 + int64_t(kWave) * it;
-      if (vi < vpr) score_vec<DT, RESIDUAL>(wt[it], RESIDUAL ? wd[it] : wt[it], vi, dp, best);
+      for (int it = 0; it < kSampleIters; ++it) {
+        const int64_t vi = vi0 + int64_t(kWave) * it;
+        if (vi < vpr)
+          score_vec_filtered<DT, RESIDUAL>(wt[it], RESIDUAL ? wd[it] : wt[it], vi, dp, thr, best);
+        float m = best.k2;
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off, kWave));
+        thr = m;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < kSampleIters; ++it) {
+        const int64_t vi = vi0 + int64_t(kWave) * it;
+        if (vi < vpr) score_vec<DT, RESIDUAL>(wt[it], RESIDUAL ? wd[it] : wt[it], vi, dp, best);
+      }
     }
     return best;
   }
@@ -1165,8 +1219,10 @@ void draw_kernel(ChainArgs a) {
   dp.r = uint32_t(chain);
   dp.s0 = uint32_t(a.seed);
   dp.s1 = uint32_t(a.seed >> 32);
-  Top2 best = residual ? scan_split<DT, VEC, true>(row_t, row_d, split, a.V, dp)
-                       : scan_split<DT, VEC, false>(row_t, row_d, split, a.V, dp);
+  // the fused kernel runs one round of workgroups (latency-bound); the
+  // separate-accept path serves grids of several rounds
+  Top2 best = residual ? scan_split<DT, VEC, true, !FUSED>(row_t, row_d, split, a.V, dp)
+                       : scan_split<DT, VEC, false, !FUSED>(row_t, row_d, split, a.V, dp);
   best = wave_top2(best);
   if (lane == 0) s_top[t / kWave] = best;
   __syncthreads();

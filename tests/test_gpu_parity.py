@@ -255,6 +255,10 @@ def test_workspace_reused_across_shapes_and_calls():
     for i, s in enumerate(shapes):
         print(f"[case] shared workspace call {i}: {s}", flush=True)
         w = workloads.make("c3", seed=i, temps=("choice", (0.0, 0.3, 1.0)), **s)
+        if i == 2:  # random bytes left by some other user of the memory
+            gen = torch.Generator(device=device()).manual_seed(11)
+            ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=device(),
+                                   generator=gen))
         shared = step_on_gpu(w, ws=ws)
         fresh = step_on_gpu(w)
         for k, v in fresh.items():
