@@ -7,7 +7,9 @@ before timing.
 
 Prints one JSON line: verified draft tokens/s (B*gamma per step) and the HBM
 roofline of the dominant kernel, plus the fp64 CPU oracle timed on a bounded
-sample as a reported baseline. `per_config` adds every workload (C1-C5, and the
+sample as a reported baseline, and `parity`: per workload, the chains whose
+accept length or token differ from the oracle's, and the chains left out
+because a decision lies within 1e-6 of its threshold. `per_config` adds every workload (C1-C5, and the
 accept test alone on C4's log-probabilities) timed cold: before each of the
 timed reps a 512 MiB buffer is rewritten, which evicts the 256 MB last-level
 cache and the L2s, and HIP events bracket the step alone (median, p10, p90).
@@ -78,33 +80,87 @@ def stacked_inputs(w, dev):
     return buf, buf[:, : g + 1], buf[:, g + 1:].unsqueeze(1)
 
 
-def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 300) -> dict:
-    """The oracle as it is, on the host's cores: one thread per slice of batch rows
-    (NumPy releases the GIL inside its array operations), whole steps repeated
-    until min_seconds have passed."""
+def _oracle_rows(w, rows):
     import oracle
 
+    return oracle.verify(w.target[rows], w.draft[rows], w.tokens[rows], w.temperature[rows],
+                         w.seed, w.pos0[rows], batch_index=rows, dtype=w.dtype)
+
+
+def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 300):
+    """The oracle as it is, on the host's cores: one thread per slice of batch rows
+    (NumPy releases the GIL inside its array operations), whole steps repeated
+    until min_seconds have passed. Returns the figure and the last step's oracle
+    accept lengths, tokens and flags."""
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     slices = [r for r in np.array_split(np.arange(w.B), threads) if len(r)]
-
-    def run(rows):
-        return oracle.verify(w.target[rows], w.draft[rows], w.tokens[rows], w.temperature[rows],
-                             w.seed, w.pos0[rows], batch_index=rows, dtype=w.dtype)
 
     reps, t0 = 0, time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(slices)) as ex:
         while reps < max_reps:
-            list(ex.map(run, slices))
+            outs = list(ex.map(lambda r: _oracle_rows(w, r), slices))
             reps += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
     dt = (time.perf_counter() - t0) / reps
+    ref = {k: np.concatenate([o[k] for o in outs]) for k in ("accept_len", "out_token", "flagged")}
     return {"value": w.B * w.K * w.gamma / dt, "unit": "tokens/s", "cores": len(slices),
             "kind": "oracle",
             "sample": f"{reps} full step(s) of the benchmark workload ({w.B} chains, "
                       f"{w.B * w.K * w.gamma} draft tokens), NumPy float64, one thread per "
                       f"slice of batch rows",
-            "seconds_per_step": dt, "gbps": algorithmic_bytes(w) / dt / 1e9}
+            "seconds_per_step": dt, "gbps": algorithmic_bytes(w) / dt / 1e9}, ref
+
+
+# Batch rows of each workload whose chains the parity count covers (all of the small
+# ones; a seeded sample of the large ones, so the oracle finishes in seconds).
+PARITY_ROWS = {"c4": 32, "c5": 16}
+
+
+def parity_rows(w) -> np.ndarray:
+    n = PARITY_ROWS.get(w.name)
+    if n is None or n >= w.B:
+        return np.arange(w.B)
+    return np.sort(np.random.default_rng(1234).choice(w.B, n, replace=False))
+
+
+def parity_sample(w, out) -> dict:
+    """What the oracle needs to check a GPU step on parity_rows(w): the rows' inputs and
+    the GPU's accept lengths and tokens for them."""
+    rows = parity_rows(w)
+    return {"rows": rows, "B": w.B, "name": w.name, "seed": w.seed, "dtype": w.dtype,
+            "target": w.target[rows], "draft": w.draft[rows], "tokens": w.tokens[rows],
+            "temperature": w.temperature[rows], "pos0": w.pos0[rows],
+            "accept_len": out.accept_len.cpu().numpy()[rows],
+            "out_token": out.out_token.cpu().numpy()[rows]}
+
+
+def parity_count(gpu_n, gpu_y, ref, rows_note: str) -> dict:
+    """Mismatches of the GPU step against the oracle on chains whose decisions are not
+    within 1e-6 of a threshold, and the number of such excluded (flagged) chains."""
+    ok = ~ref["flagged"]
+    return {"chains": int(ok.size), "rows": rows_note,
+            "accept_len_mismatches": int(((gpu_n != ref["accept_len"]) & ok).sum()),
+            "out_token_mismatches": int(((gpu_y != ref["out_token"]) & ok).sum()),
+            "flagged_excluded": int(ref["flagged"].sum())}
+
+
+def parity_of_samples(samples: dict) -> dict:
+    import oracle
+
+    res = {}
+    for name, smp in samples.items():
+        rows = smp["rows"]
+        ref = oracle.verify(smp["target"], smp["draft"], smp["tokens"], smp["temperature"],
+                            smp["seed"], smp["pos0"], batch_index=rows, dtype=smp["dtype"])
+        note = "all" if rows.size == smp["B"] else f"{rows.size} of {smp['B']} (seeded sample)"
+        res[name] = parity_count(smp["accept_len"], smp["out_token"], ref, note)
+    return res
+
+
+def progress(msg: str) -> None:
+    """One line on stderr as each phase ends (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def device_logits(raw: np.ndarray, dtype: str, dev) -> torch.Tensor:
@@ -132,8 +188,9 @@ def cold_times_us(fn, reps: int, warmup: int, scratch: torch.Tensor, stream) -> 
     return [1e3 * a.elapsed_time(b) for a, b in ev]
 
 
-def per_config(names, reps: int, warmup: int, dev) -> dict:
-    """Every workload's step timed cold; C4 also times the accept test alone."""
+def per_config(names, reps: int, warmup: int, dev, samples: dict | None = None) -> dict:
+    """Every workload's step timed cold; C4 also times the accept test alone. With
+    `samples`, each workload's parity_sample of its last timed step is kept there."""
     stream = torch.cuda.current_stream(dev)
     scratch = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
     res = {}
@@ -163,6 +220,9 @@ def per_config(names, reps: int, warmup: int, dev) -> dict:
                  "bytes_min": nbytes, "hbm_gbps": nbytes / (med * 1e-6) / 1e9,
                  "hbm_frac_of_peak": nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                  "device_error": int(plan.out.device_error.item())}
+        if samples is not None:
+            samples[name] = parity_sample(w, plan.out)
+        progress(f"{name}: step {med:.1f} us cold")
         # the acceptance probability and accept-length law of the same step's rows
         lz_t = plan.out.lnZ_target.clone()
         lz_d = torch.nan_to_num(plan.out.lnZ_draft, nan=0.0)
@@ -251,6 +311,7 @@ def main() -> int:
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
+    progress(f"timed region: {args.steps} steps, {1e3 * ms_per_step:.1f} us per step")
 
     # Context only (not `value`): two independent batches alternating on two streams,
     # so that one batch's draws can overlap the other's streaming (as two micro-batches
@@ -268,20 +329,22 @@ def main() -> int:
         torch.cuda.synchronize(dev)
         two_stream_ms = 1e3 * (time.perf_counter() - t0) / args.steps
 
-    # Dominant kernel: the streaming normaliser over the same 1088 rows, timed with
-    # HIP events on the launch stream (the normalise entry point launches it plus a
-    # finalise of eight lanes per row).
-    ws = sv.workspace(w.B, 0, 2 * w.gamma, w.V, sv.SV_BF16, dev)
+    # Dominant kernel: the streaming normaliser inside the same steps, timed with HIP
+    # events that the library records on its launch stream just before and after that
+    # kernel (the same steps again, after the timed region, so the event records do
+    # not touch `value`).
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
-    for i in range(args.warmup):
-        sv.specverify_normalize(copies[i % len(copies)][0], temp, ws=ws)
+    for a, b in ev:  # the events exist once recorded
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize(dev)
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        sv.specverify_normalize(copies[i % len(copies)][0], temp, ws=ws)
-        ev[i][1].record(stream)
+        sv.time_next_stream_kernel(*ev[i])
+        plans[i % len(plans)]()
     torch.cuda.synchronize(dev)
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    progress(f"stream kernel: {1e3 * kern_ms:.1f} us per launch")
 
     if args.copy_calibration:
         # A plain device copy of known size, for scaling the HBM byte counters.
@@ -294,7 +357,9 @@ def main() -> int:
     out = plans[0].out
     err = int(out.device_error.item())
     bytes_min = algorithmic_bytes(w)
-    kernel_bytes = w.B * (2 * w.gamma + 1) * w.V * w.bytes_per_logit
+    # every target row and every sampled batch row's draft rows, read once
+    kernel_bytes = (w.B * (w.gamma + 1) + int((w.temperature > 0).sum()) * w.K * w.gamma) \
+        * w.V * w.bytes_per_logit
     achieved = kernel_bytes / (kern_ms * 1e-3) / 1e9
     tokens_per_step = w.B * w.K * w.gamma
     value = tokens_per_step / (ms_per_step * 1e-3)
@@ -324,17 +389,29 @@ def main() -> int:
         "bytes_min_per_step": bytes_min,
         "accepted_tokens_per_step": int((out.accept_len.clamp(min=0) + 1).sum().item()),
         "device_error": err,
-        "roofline": {"bound": "hbm", "kernel": "stream_kernel (+finalize_rows_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "stream_kernel",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(),
-                     "bytes_per_launch": kernel_bytes, "avg_launch_ms": kern_ms},
+                     "bytes_per_launch": kernel_bytes, "avg_launch_ms": kern_ms,
+                     "timing": "HIP events recorded by the library around the stream kernel "
+                               f"inside {args.steps} steps"},
     }
+    gpu_n = out.accept_len.cpu().numpy()
+    gpu_y = out.out_token.cpu().numpy()
+    samples = {} if not args.no_cpu else None
     if args.per_config != "none":
         names = (list(workloads.CONFIGS) if args.per_config == "all"
                  else [n for n in args.per_config.split(",") if n])
-        line["per_config"] = per_config(names, args.reps, 10, dev)
+        line["per_config"] = per_config(names, args.reps, 10, dev, samples)
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(w)
+        # the oracle's leg: its timing, and the parity of the GPU steps above against it
+        line["cpu_baseline"], ref = cpu_baseline(w)
+        progress("oracle timed")
+        parity = {"c3_timed_step": parity_count(gpu_n, gpu_y, ref, "all")}
+        parity.update(parity_of_samples(samples))
+        line["parity"] = parity
+    else:
+        line["parity"] = None
     print(json.dumps(line), flush=True)
     return 0
 

@@ -64,6 +64,7 @@ _SIGNATURES = {
                                        _P]),
     "specverify_status_string": (ctypes.c_char_p, [_INT]),
     "specverify_version": (_INT, []),
+    "specverify_time_next_stream_kernel": (_INT, [_P, _P]),
 }
 
 
@@ -441,6 +442,17 @@ def step_reward(accept_len, gamma: int) -> float:
     _check(load_library().specverify_step_reward(arr.data_ptr(), arr.numel(), gamma,
                                                   ctypes.byref(out)), "specverify_step_reward")
     return out.value
+
+
+def time_next_stream_kernel(before: torch.cuda.Event | None, after: torch.cuda.Event | None) -> None:
+    """The next step or normalise call on this thread records `before` / `after` around its
+    streaming kernel (timing events; each must have been recorded once so that it exists)."""
+    b = None if before is None else before.cuda_event
+    a = None if after is None else after.cuda_event
+    if (before is not None and not b) or (after is not None and not a):
+        raise SpecVerifyError("record the events once before handing them to the library")
+    _check(load_library().specverify_time_next_stream_kernel(b, a),
+           "specverify_time_next_stream_kernel")
 
 
 def version() -> int:

@@ -37,6 +37,7 @@
 // atomics: results are bit-deterministic.
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <atomic>
 #include <climits>
@@ -2065,16 +2066,45 @@ int check_dtype(int dtype) { return (dtype == SV_F32 || dtype == SV_BF16) ? SV_O
 int esize(int dtype) { return dtype == SV_BF16 ? 2 : 4; }
 int launch_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP; }
 
+// ev0 / ev1 (timing hook): events the launch itself marks with the kernel's
+// start and end (hipExtLaunchKernel), so their elapsed time is the kernel's
+// execution alone, as a profiler reports it.
 template <int DT, bool VEC, bool ARGMAX_ALL>
-void launch_stream_t(const StreamArgs& sa, hipStream_t st) {
+void launch_stream_t(const StreamArgs& sa, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   int64_t grid = stream_blocks<DT, VEC, ARGMAX_ALL>();
   const int64_t need = (sa.nrows * sa.cpr + kStreamWaves - 1) / kStreamWaves;
   if (grid > need) grid = need;
-  hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(grid)),
-                     dim3(kStreamBlock), 0, st, sa);
+  if (ev0)
+    hipExtLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(grid)),
+                          dim3(kStreamBlock), 0, st, ev0, ev1, 0u, sa);
+  else
+    hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(grid)),
+                       dim3(kStreamBlock), 0, st, sa);
 }
 
+void launch_stream_dt(int dtype, bool vec, bool argmax_all, const StreamArgs& sa, hipStream_t st,
+                      hipEvent_t e0, hipEvent_t e1) {
+  if (dtype == SV_BF16) {
+    if (vec) argmax_all ? launch_stream_t<SV_BF16, true, true>(sa, st, e0, e1)
+                        : launch_stream_t<SV_BF16, true, false>(sa, st, e0, e1);
+    else argmax_all ? launch_stream_t<SV_BF16, false, true>(sa, st, e0, e1)
+                    : launch_stream_t<SV_BF16, false, false>(sa, st, e0, e1);
+    return;
+  }
+  if (vec) argmax_all ? launch_stream_t<SV_F32, true, true>(sa, st, e0, e1)
+                      : launch_stream_t<SV_F32, true, false>(sa, st, e0, e1);
+  else argmax_all ? launch_stream_t<SV_F32, false, true>(sa, st, e0, e1)
+                  : launch_stream_t<SV_F32, false, false>(sa, st, e0, e1);
+}
+
+// Events the next streaming-kernel launch of this host thread records around
+// itself (specverify_time_next_stream_kernel); taken, and so cleared, by it.
+thread_local hipEvent_t t_ev_before = nullptr;
+thread_local hipEvent_t t_ev_after = nullptr;
+
 void launch_stream(int dtype, bool vec, bool argmax_all, StreamArgs sa, hipStream_t st) {
+  const hipEvent_t ev_before = t_ev_before, ev_after = t_ev_after;
+  t_ev_before = t_ev_after = nullptr;
   // chunk indices are below 2^31 (stream_chunks_ok): the kernel divides by
   // multiply-shift
   const int64_t kg = sa.rs.K * sa.rs.G;
@@ -2082,17 +2112,7 @@ void launch_stream(int dtype, bool vec, bool argmax_all, StreamArgs sa, hipStrea
   sa.by_p = make_fastdiv(uint32_t(sa.rs.P));
   sa.by_kg = make_fastdiv(uint32_t(kg > 0 ? kg : 1));
   sa.by_g = make_fastdiv(uint32_t(sa.rs.G > 0 ? sa.rs.G : 1));
-  if (dtype == SV_BF16) {
-    if (vec) argmax_all ? launch_stream_t<SV_BF16, true, true>(sa, st)
-                        : launch_stream_t<SV_BF16, true, false>(sa, st);
-    else argmax_all ? launch_stream_t<SV_BF16, false, true>(sa, st)
-                    : launch_stream_t<SV_BF16, false, false>(sa, st);
-    return;
-  }
-  if (vec) argmax_all ? launch_stream_t<SV_F32, true, true>(sa, st)
-                      : launch_stream_t<SV_F32, true, false>(sa, st);
-  else argmax_all ? launch_stream_t<SV_F32, false, true>(sa, st)
-                  : launch_stream_t<SV_F32, false, false>(sa, st);
+  launch_stream_dt(dtype, vec, argmax_all, sa, st, ev_before, ev_after);
 }
 
 // Workgroups of the fused draw kernel resident on the device at once (cached per
@@ -2706,6 +2726,13 @@ int specverify_branch_prune(const float* logq, int64_t B, int64_t K, int64_t gam
   hipLaunchKernelGGL(branch_prune_kernel, dim3(unsigned((B + kBlock - 1) / kBlock)), dim3(kBlock),
                      0, st, logq, B, K, gamma, log_tau, keep, keep_mask, prefix_len, conf);
   return launch_status();
+}
+
+int specverify_time_next_stream_kernel(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return SV_EINVAL;
+  t_ev_before = static_cast<hipEvent_t>(before);
+  t_ev_after = static_cast<hipEvent_t>(after);
+  return SV_OK;
 }
 
 int specverify_version(void) { return 200; }

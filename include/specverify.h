@@ -384,6 +384,21 @@ int specverify_branch_prune(const float* logq, int64_t B, int64_t K, int64_t gam
                             double log_tau, int64_t keep, int32_t* keep_mask,
                             int32_t* prefix_len, double* conf, void* stream);
 
+/*
+ * Measurement hook; results are unaffected. The next call on the calling host
+ * thread that launches the streaming kernel (specverify_step,
+ * specverify_step_noalloc, specverify_normalize) launches it with hipExtLaunchKernel,
+ * which marks `before` with the kernel's start and `after` with its end, so
+ * that hipEventElapsedTime(before, after) is the kernel's execution time
+ * (a profiler's per-kernel duration, read live). One-shot: that launch clears
+ * the hook; a call that fails its checks before launching leaves it set.
+ * before, after: hipEvent_t handles the caller created (with timing) on the
+ * device of the call and keeps alive until the call's stream has passed them;
+ * NULL, NULL clears the hook. Pure host function.
+ * Status: SV_EINVAL when exactly one of the two is NULL.
+ */
+int specverify_time_next_stream_kernel(void* before, void* after);
+
 /* Static host string describing a status code. */
 const char* specverify_status_string(int status);
 

@@ -35,6 +35,7 @@ def test_exports_every_declared_symbol():
                           "specverify_bandit_select", "specverify_bandit_update",
                           "specverify_bandit_stats", "specverify_step_reward",
                           "specverify_branch_prune",
+                          "specverify_time_next_stream_kernel",
                           "specverify_status_string", "specverify_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -46,6 +47,13 @@ def test_version_and_status_strings():
     assert lib.specverify_version() >= 100
     for code in (0, -1, -2, -3, -4, -5, 99):
         assert lib.specverify_status_string(code)
+
+
+def test_timing_hook_needs_both_events_or_neither():
+    lib = sv.load_library()
+    assert lib.specverify_time_next_stream_kernel(8, None) == -1
+    assert lib.specverify_time_next_stream_kernel(None, 8) == -1
+    assert lib.specverify_time_next_stream_kernel(None, None) == 0   # clears
 
 
 def test_workspace_sizes():
