@@ -1595,6 +1595,7 @@ struct TopFArgs {
   int64_t ftot;
   int32_t* cand;         // [B*K][ftot]
   float* cand_w;         // [B*K][ftot] or null
+  int bonus_last;        // workgroup order: rows j < gamma first, then the j = gamma rows
 };
 
 __device__ __forceinline__ bool topf_before(float sa, int32_t ia, float sb, int32_t ib) {
@@ -1700,9 +1701,14 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   const RowSet& rs = a.rs;
   const int64_t G = rs.G;
-  const int64_t row = blockIdx.x;
-  const int64_t chain = row / (G + 1);
-  const int j = int(row - chain * (G + 1));
+  // bonus_last: the rows j < gamma (two logit rows each) first and the j = gamma
+  // rows (one) last, so that where some CUs hold one workgroup more than others
+  // (a grid of one round) the extra ones are the cheaper rows; otherwise
+  // chain-major.
+  const int64_t x = blockIdx.x;
+  const int64_t nres = a.bonus_last ? rs.B * rs.K * G : 0;
+  const int64_t chain = x < nres ? x / G : a.bonus_last ? x - nres : x / (G + 1);
+  const int j = x < nres ? int(x - chain * G) : a.bonus_last ? int(G) : int(x - chain * (G + 1));
   const int F = a.fan[j];
   if (F == 0) return;
   const int tid = threadIdx.x;
@@ -2689,6 +2695,9 @@ int specverify_residual_topf(const void* target_logits, const void* draft_logits
   // latency, above it occupancy bounds the rate.
   const int64_t cus = device_cus();
   const bool wide = rows >= cus && rows <= int64_t(kTopFWideRowsPerCU) * cus;
+  // at most three workgroups per CU: one round (C3: 126 vs 139 us; grids of
+  // several rounds measured slower in this order)
+  ta.bonus_last = rows <= 3 * cus ? 1 : 0;
   if (dtype == SV_BF16) {
     if (vec) launch_topf<SV_BF16, true>(wide, grid, st, ta);
     else launch_topf<SV_BF16, false>(wide, grid, st, ta);
