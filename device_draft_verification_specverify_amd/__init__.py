@@ -14,12 +14,15 @@ from dataclasses import dataclass
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(HERE, "libspecverify.so")
+# SPECVERIFY_LIBRARY selects another build of the library (e.g. the one with
+# device-side index checks, libspecverify_checked.so).
+LIBRARY = os.environ.get("SPECVERIFY_LIBRARY") or os.path.join(HERE, "libspecverify.so")
 
 SV_F32 = 0
 SV_BF16 = 1
 SV_OK = 0
 SV_ESCRATCH = -6
+SV_ENOCHECKS = -7
 NOALLOC_SCRATCH_BYTES = 32 << 20
 SV_ERR_TOKEN = 1
 SV_ERR_TEMP = 2
@@ -65,6 +68,7 @@ _SIGNATURES = {
     "specverify_status_string": (ctypes.c_char_p, [_INT]),
     "specverify_version": (_INT, []),
     "specverify_time_next_stream_kernel": (_INT, [_P, _P]),
+    "specverify_check_count": (_INT, [_P, _INT]),
 }
 
 
@@ -453,6 +457,17 @@ def time_next_stream_kernel(before: torch.cuda.Event | None, after: torch.cuda.E
         raise SpecVerifyError("record the events once before handing them to the library")
     _check(load_library().specverify_time_next_stream_kernel(b, a),
            "specverify_time_next_stream_kernel")
+
+
+def check_count(reset: bool = False) -> int | None:
+    """Failed device-side index checks so far on the current device, or None when the
+    loaded library was built without them (the product build)."""
+    n = ctypes.c_uint32()
+    st = load_library().specverify_check_count(ctypes.byref(n), int(reset))
+    if st == SV_ENOCHECKS:
+        return None
+    _check(st, "specverify_check_count")
+    return int(n.value)
 
 
 def version() -> int:

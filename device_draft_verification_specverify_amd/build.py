@@ -15,6 +15,9 @@ SOURCE = os.path.join(HERE, "csrc", "specverify.hip")
 HOST_SOURCES = [os.path.join(HERE, "csrc", "bandit.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libspecverify.so")
+# The same sources with device-side index checks (-DSV_DEVICE_CHECKS): a debug
+# build for running the GPU tests with every work unit's indices checked.
+CHECKED_LIBRARY = os.path.join(HERE, "libspecverify_checked.so")
 ARCH = "gfx950"
 
 # Packed FP32 instructions stay off: the compiler must not form them.
@@ -38,11 +41,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile the HIP source into LIBRARY (always recompiles). Returns the path."""
-    tmp = LIBRARY + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, SOURCE, *HOST_SOURCES,
-           "-o", tmp]
+def build(verbose: bool = False, extra_flags: list[str] | None = None,
+          checked: bool = False) -> str:
+    """Compile the HIP source into LIBRARY, or CHECKED_LIBRARY with the device-side
+    index checks (always recompiles). Returns the path."""
+    out = CHECKED_LIBRARY if checked else LIBRARY
+    tmp = out + ".tmp"
+    flags = [*HIP_FLAGS, *(extra_flags or []), *(["-DSV_DEVICE_CHECKS"] if checked else [])]
+    cmd = [hipcc(), *flags, "-I", INCLUDE, SOURCE, *HOST_SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,9 +56,9 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
     if verbose and res.stderr.strip():
         print(res.stderr, file=sys.stderr)
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, checked="--checked" in sys.argv[1:]))

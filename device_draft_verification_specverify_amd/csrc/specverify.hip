@@ -150,6 +150,22 @@ __device__ __forceinline__ double log_uniform_d(double u) {
 }
 
 // ---------------------------------------------------------------------------
+// Device-side index checks (a build with -DSV_DEVICE_CHECKS): a work unit checks
+// the indices it derived against the sizes it was launched with before it
+// touches memory; a failed check is counted in sv_check_count (read by
+// specverify_check_count) and the unit is skipped. In the product build sv_ok
+// is true and the checks fold away.
+#ifdef SV_DEVICE_CHECKS
+__device__ unsigned int sv_check_count;
+__device__ __forceinline__ bool sv_ok(bool ok) {
+  if (!ok) atomicAdd(&sv_check_count, 1u);
+  return ok;
+}
+#else
+__device__ __forceinline__ bool sv_ok(bool) { return true; }
+#endif
+
+// ---------------------------------------------------------------------------
 // Logit access. A "vector" is 8 consecutive logits starting at a multiple of 8.
 template <int DT>
 __device__ __forceinline__ float load_one(const void* row, int64_t e) {
@@ -530,12 +546,13 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
     const void* row;
     int64_t b;
     int64_t slot = rho;  // partials sit by batch row: target rows, then draft rows (b, k, j)
-    bool is_draft;
+    bool is_draft, unit_ok;
     if (rho < BP) {
       b = fast_div(uint32_t(rho), a.by_p);
       const int64_t j = rho - b * rs.P;
       row = row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj);
       is_draft = false;
+      unit_ok = sv_ok(b < rs.B && j < rs.P);
     } else {
       const int64_t d = rho - BP;
       const int64_t sidx = fast_div(uint32_t(d), a.by_kg);
@@ -546,11 +563,13 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
       row = row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj);
       is_draft = true;
       slot = BP + b * KG + rem;
+      unit_ok = sv_ok(b < rs.B && k < rs.K && j < rs.G);
     }
+    unit_ok = unit_ok && sv_ok(slot < BP + rs.B * KG && c - rho * a.cpr < a.cpr && v0 < v1);
     // In compact mode every streamed draft row belongs to a sampled batch row,
     // so the chunk's loads go out before the temperature arrives; otherwise a
     // greedy row's draft logits are skipped, never read.
-    const bool skip = is_draft && !a.compact && !(rs.temp[b] > 0.0f);
+    const bool skip = !unit_ok || (is_draft && !a.compact && !(rs.temp[b] > 0.0f));
     RowPartial out{-INFINITY, INT_MAX, 0.0};
     if (!skip) {
       RawVec<DT> r[CL];
@@ -628,7 +647,7 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
         out = RowPartial{am, ai, __ballot(nan_seen != 0) ? double(NAN) : 0.0};
       }
     }
-    if (lane == 0) a.part[slot * a.cpr + (c - rho * a.cpr)] = out;
+    if (lane == 0 && unit_ok) a.part[slot * a.cpr + (c - rho * a.cpr)] = out;
     c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(next));
   }
 }
@@ -1035,6 +1054,11 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
   const int G = int(rs.G);
   const int P = G + 1;
   const int t = threadIdx.x;
+  if (!sv_ok(chain < rs.B * rs.K)) {  // uniform in the workgroup
+    if (t == 0) *s_n = -1;
+    __syncthreads();
+    return;
+  }
   const float T = rs.temp[b];
   const bool sampled = T > 0.0f;
   const bool greedy = T == 0.0f;
@@ -1203,6 +1227,7 @@ void draw_kernel(ChainArgs a) {
     lzt_c = ci.lzt;
     lzd_c = ci.lzd;
   }
+  if (!sv_ok(n <= G && chain < rs.B * rs.K && split < a.nsplit)) return;
   const int64_t b = FUSED ? int64_t(uint32_t(chain) / uint32_t(rs.K)) : int64_t(fast_div(uint32_t(chain), a.by_k));
   const int64_t k = chain - b * rs.K;
   const int t = threadIdx.x;
@@ -1291,7 +1316,7 @@ __global__ __launch_bounds__(kWave) void finish_kernel(const void* tgt, int64_t 
   const int64_t chain = blockIdx.x;
   const ChainInfo ci = info[chain];
   const int n = ci.n;
-  if (n < 0) return;
+  if (n < 0 || !sv_ok(n <= G)) return;
   const int lane = threadIdx.x;
   double best = -INFINITY;
   int32_t id = INT_MAX;
@@ -1411,6 +1436,10 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
     const int64_t j = bj - b * G;
     const int64_t v0 = chunk * cv;
     const int64_t v1 = v0 + cv < a.vpr ? v0 + cv : a.vpr;
+    if (!sv_ok(b < rs.B && j < G && chunk < a.cpr && v0 < v1)) {
+      c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(next));
+      continue;
+    }
     const float T = rs.temp[b];
     const bool sampled = T > 0.0f;
     const void* trow = row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj);
@@ -1713,6 +1742,7 @@ __global__ __launch_bounds__(kTopFBlock) void topf_kernel(TopFArgs a) {
   const int64_t nres = a.bonus_last ? rs.B * rs.K * G : 0;
   const int64_t chain = x < nres ? x / G : a.bonus_last ? x - nres : x / (G + 1);
   const int j = x < nres ? int(x - chain * G) : a.bonus_last ? int(G) : int(x - chain * (G + 1));
+  if (!sv_ok(chain < rs.B * rs.K && j >= 0 && j <= G)) return;
   const int F = a.fan[j];
   if (F == 0) return;
   const int tid = threadIdx.x;
@@ -2567,6 +2597,7 @@ const char* specverify_status_string(int status) {
     case SV_ESCRATCH:
       return "sizes need more scratch than specverify_step_noalloc holds "
              "(SV_NOALLOC_SCRATCH_BYTES); use specverify_step with a workspace";
+    case SV_ENOCHECKS: return "library built without device-side index checks";
     default: return "unknown status";
   }
 }
@@ -2739,6 +2770,24 @@ int specverify_branch_prune(const float* logq, int64_t B, int64_t K, int64_t gam
   hipLaunchKernelGGL(branch_prune_kernel, dim3(unsigned((B + kBlock - 1) / kBlock)), dim3(kBlock),
                      0, st, logq, B, K, gamma, log_tau, keep, keep_mask, prefix_len, conf);
   return launch_status();
+}
+
+int specverify_check_count(uint32_t* count, int reset) {
+#ifdef SV_DEVICE_CHECKS
+  if (!count) return SV_EINVAL;
+  if (hipMemcpyFromSymbol(count, HIP_SYMBOL(sv_check_count), sizeof(uint32_t)) != hipSuccess)
+    return SV_EHIP;
+  if (reset) {
+    const uint32_t zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(sv_check_count), &zero, sizeof zero) != hipSuccess)
+      return SV_EHIP;
+  }
+  return SV_OK;
+#else
+  (void)count;
+  (void)reset;
+  return SV_ENOCHECKS;
+#endif
 }
 
 int specverify_time_next_stream_kernel(void* before, void* after) {

@@ -71,6 +71,8 @@ extern "C" {
 #define SV_EHIP (-5)       /* a kernel launch failed                         */
 #define SV_ESCRATCH (-6)   /* specverify_step_noalloc: sizes need more scratch
                               than SV_NOALLOC_SCRATCH_BYTES                  */
+#define SV_ENOCHECKS (-7)  /* specverify_check_count: the library was built
+                              without device-side index checks               */
 
 /* Device scratch held by specverify_step_noalloc on every GPU it runs on. */
 #define SV_NOALLOC_SCRATCH_BYTES (32u << 20)
@@ -398,6 +400,20 @@ int specverify_branch_prune(const float* logq, int64_t B, int64_t K, int64_t gam
  * Status: SV_EINVAL when exactly one of the two is NULL.
  */
 int specverify_time_next_stream_kernel(void* before, void* after);
+
+/*
+ * Debugging aid. A library built with device-side index checks
+ * (build.py --checked: libspecverify_checked.so, -DSV_DEVICE_CHECKS) has every
+ * work unit of every kernel check the indices it derived (batch row, branch,
+ * position, chunk, split, accept length) against the sizes it was launched
+ * with before touching memory; a failed check is counted on the device and
+ * the unit is skipped. This call copies the count of the current device into
+ * *count and, when reset is non-zero, sets it to zero. Blocking (a device copy
+ * on the null stream): call after the work to be checked has completed.
+ * Status: SV_ENOCHECKS in a build without the checks (the product library),
+ * SV_EINVAL (count NULL), SV_EHIP.
+ */
+int specverify_check_count(uint32_t* count, int reset);
 
 /* Static host string describing a status code. */
 const char* specverify_status_string(int status);

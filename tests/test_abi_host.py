@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
                           "specverify_bandit_select", "specverify_bandit_update",
                           "specverify_bandit_stats", "specverify_step_reward",
                           "specverify_branch_prune",
-                          "specverify_time_next_stream_kernel",
+                          "specverify_time_next_stream_kernel", "specverify_check_count",
                           "specverify_status_string", "specverify_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -54,6 +54,14 @@ def test_timing_hook_needs_both_events_or_neither():
     assert lib.specverify_time_next_stream_kernel(8, None) == -1
     assert lib.specverify_time_next_stream_kernel(None, 8) == -1
     assert lib.specverify_time_next_stream_kernel(None, None) == 0   # clears
+
+
+def test_check_count_needs_the_checked_build():
+    lib = sv.load_library()
+    n = ctypes.c_uint32(7)
+    if os.path.basename(sv.LIBRARY) == "libspecverify.so":
+        assert lib.specverify_check_count(ctypes.byref(n), 0) == sv.SV_ENOCHECKS
+        assert sv.check_count() is None
 
 
 def test_workspace_sizes():

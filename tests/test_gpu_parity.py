@@ -408,3 +408,16 @@ def test_empty_residual_support_draws_from_p_unmasked():
         print(f"[parity] empty support: {int(robust.sum())} of {w.B} compared", flush=True)
         assert robust.sum() >= w.B - 1
         assert np.array_equal(got[robust, 0], tok[robust, 0]), (got.ravel(), tok.ravel())
+
+
+def test_the_named_checked_build_is_the_one_loaded():
+    """Under SPECVERIFY_LIBRARY=<libspecverify_checked.so> every GPU test ends with a
+    zero count of failed device-side index checks (tests/conftest.py); this confirms
+    that the counting build is the one in use."""
+    import os
+
+    named = os.environ.get("SPECVERIFY_LIBRARY")
+    if not named:
+        pytest.skip("the product build is loaded (SPECVERIFY_LIBRARY unset)")
+    assert os.path.samefile(sv.LIBRARY, named)
+    assert sv.check_count() is not None, "the named library has no device-side index checks"
