@@ -51,18 +51,20 @@ def test_step_matches_oracle_c3_full():
 
 def test_step_matches_oracle_c4_full_sampled_rows():
     w = workloads.make("c4")
-    print("[case] c4 full B=256, oracle on 40 rows", flush=True)
+    print("[case] c4 full B=256, oracle on 64 rows", flush=True)
     gpu = step_on_gpu(w)
-    rows = np.concatenate([np.arange(16), np.random.default_rng(4).choice(np.arange(16, 256), 24,
+    rows = np.concatenate([np.arange(16), np.random.default_rng(4).choice(np.arange(16, 256), 48,
                                                                           replace=False)])
     _report("c4", compare_step(gpu, _ref(w, rows), w.temperature, rows))
 
 
 def test_step_matches_oracle_c5_full_sampled_rows():
     w = workloads.make("c5")
-    print("[case] c5 full B=512 K=4, oracle on 10 rows", flush=True)
+    rows = np.unique(np.concatenate([[0, 1, 77, 128, 255, 256, 300, 411, 510, 511],
+                                     np.random.default_rng(5).choice(512, 22, replace=False)]))
+    print(f"[case] c5 full B=512 K=4, oracle on {rows.size} rows ({4 * rows.size} chains)",
+          flush=True)
     gpu = step_on_gpu(w)
-    rows = np.array([0, 1, 77, 128, 255, 256, 300, 411, 510, 511])
     _report("c5", compare_step(gpu, _ref(w, rows), w.temperature, rows))
     # properties at every chain: lengths in range, corrections differ from the rejected draft
     n, y = gpu["accept_len"], gpu["out_token"]
