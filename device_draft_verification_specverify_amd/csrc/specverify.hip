@@ -1556,6 +1556,7 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
 // One wavefront per chain: alpha_j from the chunk partials (a fixed-order
 // float64 sum; greedy rows: do the two rows' lowest argmaxes agree), then the
 // accept-length law.
+constexpr int kAlphaBatch = 8;
 __global__ __launch_bounds__(kBlock) void alpha_law_kernel(const OverlapPartial* __restrict__ part,
                                                            int64_t chains, int64_t K, int64_t G,
                                                            int64_t cpr,
@@ -1569,33 +1570,52 @@ __global__ __launch_bounds__(kBlock) void alpha_law_kernel(const OverlapPartial*
   const bool sampled = T > 0.0f;
   const bool greedy = T == 0.0f;
   double reach = 1.0;  // P(n >= j), kept by every lane
-  for (int64_t j = 0; j < G; ++j) {
-    const OverlapPartial* pr = part + (chain * G + j) * cpr;
-    double s = 0.0;
-    float tm = -INFINITY, dm = -INFINITY;
-    int32_t ti = INT_MAX, di = INT_MAX;
+  // kAlphaBatch positions at a time: their partials' loads all go out before
+  // any is folded (one round of memory latency per batch, not per position)
+  for (int64_t j0 = 0; j0 < G; j0 += kAlphaBatch) {
+    double s[kAlphaBatch];
+    float tm[kAlphaBatch], dm[kAlphaBatch];
+    int32_t ti[kAlphaBatch], di[kAlphaBatch];
+#pragma unroll
+    for (int q = 0; q < kAlphaBatch; ++q) {
+      s[q] = 0.0;
+      tm[q] = dm[q] = -INFINITY;
+      ti[q] = di[q] = INT_MAX;
+    }
     for (int64_t c = lane; c < cpr; c += kWave) {
-      const OverlapPartial q = pr[c];
-      s += q.s;
-      better_max(tm, ti, q.mt, q.it);
-      better_max(dm, di, q.md, q.id);
+      OverlapPartial p[kAlphaBatch];
+#pragma unroll
+      for (int q = 0; q < kAlphaBatch; ++q)
+        if (j0 + q < G) p[q] = part[(chain * G + j0 + q) * cpr + c];
+#pragma unroll
+      for (int q = 0; q < kAlphaBatch; ++q)
+        if (j0 + q < G) {
+          s[q] += p[q].s;
+          better_max(tm[q], ti[q], p[q].mt, p[q].it);
+          better_max(dm[q], di[q], p[q].md, p[q].id);
+        }
     }
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      s += __shfl_xor(s, off, kWave);
-      const float otm = __shfl_xor(tm, off, kWave);
-      const int32_t oti = __shfl_xor(ti, off, kWave);
-      const float odm = __shfl_xor(dm, off, kWave);
-      const int32_t odi = __shfl_xor(di, off, kWave);
-      better_max(tm, ti, otm, oti);
-      better_max(dm, di, odm, odi);
+    for (int q = 0; q < kAlphaBatch; ++q) {
+      if (j0 + q >= G) break;  // uniform
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        s[q] += __shfl_xor(s[q], off, kWave);
+        const float otm = __shfl_xor(tm[q], off, kWave);
+        const int32_t oti = __shfl_xor(ti[q], off, kWave);
+        const float odm = __shfl_xor(dm[q], off, kWave);
+        const int32_t odi = __shfl_xor(di[q], off, kWave);
+        better_max(tm[q], ti[q], otm, oti);
+        better_max(dm[q], di[q], odm, odi);
+      }
+      const int64_t j = j0 + q;
+      const double aj = sampled ? s[q] : greedy ? (ti[q] == di[q] ? 1.0 : 0.0) : double(NAN);
+      if (lane == 0) {
+        alpha[chain * G + j] = aj;
+        if (law) law[chain * (G + 1) + j] = reach * (1.0 - aj);
+      }
+      reach *= aj;
     }
-    const double aj = sampled ? s : greedy ? (ti == di ? 1.0 : 0.0) : double(NAN);
-    if (lane == 0) {
-      alpha[chain * G + j] = aj;
-      if (law) law[chain * (G + 1) + j] = reach * (1.0 - aj);
-    }
-    reach *= aj;
   }
   if (lane == 0 && law) law[chain * (G + 1) + G] = reach;
 }
