@@ -1,12 +1,13 @@
 """GPU: the usage patterns of a serving loop, through the C ABI.
 
 * one workspace buffer shared by every entry point, in any order, stays valid
-  (the per-chain counters sit at a fixed place and every call leaves them zero;
-  the acceptance sweep writes after them);
+  (the per-chain counters sit at a fixed place and each call's first launch
+  zeroes the ones it counts on; the acceptance sweep writes after them);
 * two batches in flight on two streams, each with its own workspace, give the
   same outputs as one at a time;
 * a step captured in a HIP graph replays with the eager step's outputs, replay
-  after replay, with other eager work between the replays.
+  after replay, with other eager work between the replays;
+* the measurement hook marks the next streaming kernel's start and end, once.
 """
 from __future__ import annotations
 
@@ -114,3 +115,27 @@ def test_step_replays_from_a_graph():
         _same(_host(plan.out), ref)
         # eager work between replays
         sv.StepPlan(t, d, tok, temp, w.seed + i, pos0)()
+
+
+def test_timing_hook_marks_the_next_stream_kernel_once():
+    print("[case] timing hook", flush=True)
+    w = workloads.make("c3", B=16)
+    t, d, tok, temp, pos0 = _inputs(w)
+    plan = sv.StepPlan(t, d, tok, temp, w.seed, pos0)
+    st = torch.cuda.current_stream(device())
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev[:2]:
+        e.record(st)                      # the events exist once recorded
+    plan()
+    torch.cuda.synchronize()
+    ev[2].record(st)
+    sv.time_next_stream_kernel(ev[0], ev[1])
+    plan()
+    ev[3].record(st)
+    torch.cuda.synchronize()
+    kern, step = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    assert 0.0 < kern < step, (kern, step)
+    # one-shot: the next call leaves the two events where they were
+    plan()
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) == kern
