@@ -855,7 +855,10 @@ __device__ __forceinline__ double rescore(bool residual, int32_t v, float zt, fl
                           double lzd, uint32_t pos, uint32_t r, uint32_t s0, uint32_t s1) {
   if (v < 0 || v == INT_MAX) return -INFINITY;
   const Philox4 blk = philox4x32_10(uint32_t(v) >> 2, pos, r, kPurposeSample, s0, s1);
-  const double u = unit_uniform_d(blk.w[v & 3]);
+  // the word of id v by selects (an index into the block would go through scratch)
+  const uint32_t k = uint32_t(v) & 3u;
+  const uint32_t word = k == 0u ? blk.w[0] : k == 1u ? blk.w[1] : k == 2u ? blk.w[2] : blk.w[3];
+  const double u = unit_uniform_d(word);
   const double g = -log(-log_uniform_d(u));
   const double lp = double(zt) / T - lzt;
   if (!residual) return lp + g;
@@ -900,17 +903,18 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
 // (score_vec_filtered); it pays where the draws are bound by arithmetic (grids
 // of several rounds) and costs latency where a single round of workgroups is
 // bound by its dependent steps.
-template <int DT, bool VEC, bool RESIDUAL, bool FILTER>
+template <int DT, bool VEC, bool RESIDUAL, bool FILTER, int SI>
 __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d, int64_t split,
                                            int64_t V, const DrawParams& dp) {
+  constexpr int64_t kSplitVecs = int64_t(kBlock) * SI;  // vectors per split
   const int64_t vpr = (V + kVec - 1) / kVec;
-  const int64_t vi0 = split * (kSplit / kVec) +
-                      int64_t(threadIdx.x / kWave) * (kWave * kSampleIters) + (threadIdx.x & (kWave - 1));
-  const bool whole = VEC && (V % kVec == 0 || (split + 1) * (kSplit / kVec) < vpr);
+  const int64_t vi0 = split * kSplitVecs +
+                      int64_t(threadIdx.x / kWave) * (kWave * SI) + (threadIdx.x & (kWave - 1));
+  const bool whole = VEC && (V % kVec == 0 || (split + 1) * kSplitVecs < vpr);
   if (whole) {
-    RawVec<DT> wt[kSampleIters], wd[kSampleIters];
+    RawVec<DT> wt[SI], wd[SI];
 #pragma unroll
-    for (int it = 0; it < kSampleIters; ++it) {
+    for (int it = 0; it < SI; ++it) {
       const int64_t vi = vi0 + int64_t(kWave) * it;
       const int64_t vc = vi < vpr ? vi : vpr - 1;
       wt[it] = load_vec<DT, true>(row_t, vc);
@@ -920,7 +924,7 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
     if constexpr (FILTER) {
       float thr = INFINITY;  // two keys of one lane are at most thr
 #pragma unroll
-      for (int it = 0; it < kSampleIters; ++it) {
+      for (int it = 0; it < SI; ++it) {
         const int64_t vi = vi0 + int64_t(kWave) * it;
         if (vi < vpr)
           score_vec_filtered<DT, RESIDUAL>(wt[it], RESIDUAL ? wd[it] : wt[it], vi, dp, thr, best);
@@ -931,16 +935,16 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
       }
     } else {
 #pragma unroll
-      for (int it = 0; it < kSampleIters; ++it) {
+      for (int it = 0; it < SI; ++it) {
         const int64_t vi = vi0 + int64_t(kWave) * it;
         if (vi < vpr) score_vec<DT, RESIDUAL>(wt[it], RESIDUAL ? wd[it] : wt[it], vi, dp, best);
       }
     }
     return best;
   }
-  RawVec<DT> rt[kSampleIters], rd[kSampleIters];
+  RawVec<DT> rt[SI], rd[SI];
 #pragma unroll
-  for (int it = 0; it < kSampleIters; ++it) {
+  for (int it = 0; it < SI; ++it) {
     const int64_t vi = vi0 + int64_t(kWave) * it;
     const bool inside = vi < vpr;
     rt[it] = inside ? load_vec_bounded<DT, VEC>(row_t, vi, V) : neg_inf_vec<DT>();
@@ -948,11 +952,11 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
   }
   Top2 best = top2_empty();
 #pragma unroll 1
-  for (int it = 0; it < kSampleIters; ++it) {
+  for (int it = 0; it < SI; ++it) {
     const int64_t vi = vi0 + int64_t(kWave) * it;
     if (vi < vpr) score_vec<DT, RESIDUAL>(rt[0], rd[0], vi, dp, best);
 #pragma unroll
-    for (int q = 0; q + 1 < kSampleIters; ++q) {
+    for (int q = 0; q + 1 < SI; ++q) {
       rt[q] = rt[q + 1];
       rd[q] = rd[q + 1];
     }
@@ -1197,7 +1201,7 @@ __global__ __launch_bounds__(kBlock) void accept_kernel(ChainArgs a) {
 // workgroup derives n and the normalisers itself (chain_prologue); otherwise
 // (specverify_residual_sample) it reads them from given_kernel's ChainInfo. At least 4 waves per SIMD: 16 workgroups' worth of waves per CU,
 // so the usual grids run in one round.
-template <int DT, bool VEC, bool FUSED>
+template <int DT, bool VEC, bool FUSED, int SI>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void draw_kernel(ChainArgs a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
@@ -1251,8 +1255,8 @@ void draw_kernel(ChainArgs a) {
   dp.s1 = uint32_t(a.seed >> 32);
   // the fused kernel runs one round of workgroups (latency-bound); the
   // separate-accept path serves grids of several rounds
-  Top2 best = residual ? scan_split<DT, VEC, true, !FUSED>(row_t, row_d, split, a.V, dp)
-                       : scan_split<DT, VEC, false, !FUSED>(row_t, row_d, split, a.V, dp);
+  Top2 best = residual ? scan_split<DT, VEC, true, !FUSED, SI>(row_t, row_d, split, a.V, dp)
+                       : scan_split<DT, VEC, false, !FUSED, SI>(row_t, row_d, split, a.V, dp);
   best = wave_top2(best);
   if (lane == 0) s_top[t / kWave] = best;
   __syncthreads();
@@ -2191,7 +2195,7 @@ int64_t draw_resident() {
       cus <= 0)
     cus = 256;
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, draw_kernel<DT, VEC, true>, kBlock,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, draw_kernel<DT, VEC, true, kSampleIters>, kBlock,
                                                    0) != hipSuccess ||
       blocks <= 0)
     blocks = 4;
@@ -2200,21 +2204,45 @@ int64_t draw_resident() {
   return n;
 }
 
+// Draws whose grid needs many rounds of resident workgroups take splits of
+// twice the ids (half the workgroups, each scanning 8 vectors per thread): the
+// per-workgroup prologue is paid half as often, and the last round's imbalance
+// is a small part of the whole. B=512 K=4 gamma=8 (25 rounds): 1198 vs 1228 us
+// per step; B=256 K=1 gamma=4 (4 rounds) measured slower this way (137 vs 131).
+constexpr int64_t kWideRounds = 8;
+
 template <int DT, bool VEC>
-void launch_chain_finish(const ChainArgs& ca, bool given, hipStream_t st) {
+void launch_chain_finish(ChainArgs ca, bool given, hipStream_t st) {
   const int64_t chains = ca.rs.B * ca.rs.K;
+  const bool fused = !given && chains * ca.nsplit <= draw_resident<DT, VEC>();
+  // bf16 only: eight float32 vectors per thread and row do not fit the registers
+  const bool wide = DT == SV_BF16 && !fused &&
+                    chains * ca.nsplit >= kWideRounds * draw_resident<DT, VEC>();
+  if (wide) {
+    ca.nsplit = (ca.V + 2 * kSplit - 1) / (2 * kSplit);  // at most the workspace's count
+    ca.by_nsplit = make_fastdiv(uint32_t(ca.nsplit));
+  }
   const dim3 grid{unsigned(chains * ca.nsplit), 1u, 1u};
+  auto draws = [&]() {
+    if constexpr (DT == SV_BF16)
+      if (wide) {
+        hipLaunchKernelGGL((draw_kernel<DT, VEC, false, 2 * kSampleIters>), grid, dim3(kBlock), 0,
+                           st, ca);
+        return;
+      }
+    hipLaunchKernelGGL((draw_kernel<DT, VEC, false, kSampleIters>), grid, dim3(kBlock), 0, st, ca);
+  };
   if (given) {
     hipLaunchKernelGGL(given_kernel, dim3(unsigned((chains + kBlock - 1) / kBlock)), dim3(kBlock),
                        0, st, ca, chains);
-    hipLaunchKernelGGL((draw_kernel<DT, VEC, false>), grid, dim3(kBlock), 0, st, ca);
-  } else if (chains * ca.nsplit <= draw_resident<DT, VEC>()) {
+    draws();
+  } else if (fused) {
     // every split derives n itself: one launch fewer, one prologue per workgroup
-    hipLaunchKernelGGL((draw_kernel<DT, VEC, true>), grid, dim3(kBlock), 0, st, ca);
+    hipLaunchKernelGGL((draw_kernel<DT, VEC, true, kSampleIters>), grid, dim3(kBlock), 0, st, ca);
   } else {
     // more workgroups than fit at once: n per chain in its own launch
     hipLaunchKernelGGL((accept_kernel<DT>), dim3(unsigned(chains)), dim3(kBlock), 0, st, ca);
-    hipLaunchKernelGGL((draw_kernel<DT, VEC, false>), grid, dim3(kBlock), 0, st, ca);
+    draws();
   }
   if (ca.cnt) return;  // the chains' last splits picked the tokens
   const RowSet& rs = ca.rs;
