@@ -82,8 +82,8 @@ struct alignas(16) RowPartial {
   double s;
 };
 
-// Best two sampling candidates of one split, ordered by (key, id), with the
-// target and draft logits at each (so the float64 re-score reads no memory).
+// Best two sampling candidates of a wavefront or a split, ordered by (key, id),
+// with the target and draft logits at each (for the float64 re-score).
 struct Top2 {
   float k1;
   int32_t i1;
@@ -117,14 +117,20 @@ struct Philox4 {
   uint32_t w[4];
 };
 
+// a ^ b ^ c in one instruction: gfx950's three-input bitwise operation with
+// the truth table of odd parity (0x96)
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                  uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
     const uint64_t p0 = uint64_t(kPhiloxM0) * c0;
     const uint64_t p1 = uint64_t(kPhiloxM1) * c2;
-    const uint32_t n0 = uint32_t(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = uint32_t(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n0 = xor3(uint32_t(p1 >> 32), c1, k0);
+    const uint32_t n2 = xor3(uint32_t(p0 >> 32), c3, k1);
     c0 = n0;
     c1 = uint32_t(p1);
     c2 = n2;
@@ -721,21 +727,6 @@ __device__ __forceinline__ bool cand_less(float ka, int32_t ia, float kb, int32_
   return ka < kb || (ka == kb && ia < ib);
 }
 
-// Insert a candidate whose id is larger than every id already held (the ids a
-// thread visits only grow), so ties keep the earlier, lower id; no branches.
-__device__ __forceinline__ void top2_push(Top2& s, float key, int32_t id, float zt, float zd) {
-  const bool b1 = key < s.k1;
-  const bool b2 = key < s.k2;
-  s.k2 = b1 ? s.k1 : (b2 ? key : s.k2);
-  s.i2 = b1 ? s.i1 : (b2 ? id : s.i2);
-  s.t2 = b1 ? s.t1 : (b2 ? zt : s.t2);
-  s.d2 = b1 ? s.d1 : (b2 ? zd : s.d2);
-  s.k1 = b1 ? key : s.k1;
-  s.i1 = b1 ? id : s.i1;
-  s.t1 = b1 ? zt : s.t1;
-  s.d1 = b1 ? zd : s.d1;
-}
-
 // The best two of two sorted pairs, by selects only (no branches, so the
 // pair stays in registers).
 __device__ __forceinline__ Top2 top2_merge(const Top2& a, const Top2& b) {
@@ -758,25 +749,59 @@ __device__ __forceinline__ Top2 top2_merge(const Top2& a, const Top2& b) {
   return r;
 }
 
-__device__ __forceinline__ Top2 top2_empty() {
-  return Top2{INFINITY, INT_MAX, 0.0f, 0.0f, INFINITY, INT_MAX, 0.0f, 0.0f};
+// A scan's running best two, each candidate packed into one double: the key's
+// float bits above the id. Keys are +inf or positive normal floats (E_v is at
+// least -log2(1 - 2^-24) and w_v at most about 1, so a key exceeds 8e-8), which
+// makes every packed value a finite normal double, and doubles of positive sign
+// order as their bit patterns do: by key, then by id. Keeping the best two is
+// then three float64 min/max instructions per id, and the logits of the two
+// that survive the wavefront's merge are read again from the row (with_logits).
+struct Best2 {
+  double c1, c2;  // c1 <= c2
+};
+
+__device__ __forceinline__ double cand_pack(float key, int32_t id) {
+  return __hiloint2double(__float_as_int(key), id);
+}
+__device__ __forceinline__ int32_t cand_id(double c) { return __double2loint(c); }
+__device__ __forceinline__ float cand_key(double c) { return __int_as_float(__double2hiint(c)); }
+
+__device__ __forceinline__ Best2 best2_empty() {
+  const double e = cand_pack(INFINITY, INT_MAX);
+  return Best2{e, e};
 }
 
-__device__ __forceinline__ Top2 wave_top2(Top2 v) {
+__device__ __forceinline__ void best2_push(Best2& s, double c) {
+  s.c2 = fmin(s.c2, fmax(s.c1, c));
+  s.c1 = fmin(s.c1, c);
+}
+
+__device__ __forceinline__ Best2 wave_best2(Best2 v) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) {
-    Top2 o;
-    o.k1 = __shfl_xor(v.k1, off, kWave);
-    o.i1 = __shfl_xor(v.i1, off, kWave);
-    o.t1 = __shfl_xor(v.t1, off, kWave);
-    o.d1 = __shfl_xor(v.d1, off, kWave);
-    o.k2 = __shfl_xor(v.k2, off, kWave);
-    o.i2 = __shfl_xor(v.i2, off, kWave);
-    o.t2 = __shfl_xor(v.t2, off, kWave);
-    o.d2 = __shfl_xor(v.d2, off, kWave);
-    v = top2_merge(v, o);
+    const double o1 = __shfl_xor(v.c1, off, kWave);
+    const double o2 = __shfl_xor(v.c2, off, kWave);
+    v.c2 = fmin(fmax(v.c1, o1), fmin(v.c2, o2));
+    v.c1 = fmin(v.c1, o1);
   }
   return v;
+}
+
+// The wavefront's best two (every lane holds them) with their target and draft
+// logits, read again from the rows by lanes 0 and 1; ids past the row (a
+// partial last vector) read -inf, as the scan saw them. Valid in every lane.
+template <int DT>
+__device__ __forceinline__ Top2 with_logits(const Best2& b, const void* row_t, const void* row_d,
+                                            bool residual, int64_t V) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t id = cand_id(lane == 0 ? b.c1 : b.c2);
+  float zt = -INFINITY, zd = -INFINITY;
+  if (lane < 2 && id < V) {
+    zt = load_one<DT>(row_t, id);
+    if (residual) zd = load_one<DT>(row_d, id);
+  }
+  return Top2{cand_key(b.c1), cand_id(b.c1), __shfl(zt, 0, kWave), __shfl(zd, 0, kWave),
+              cand_key(b.c2), cand_id(b.c2), __shfl(zt, 1, kWave), __shfl(zd, 1, kWave)};
 }
 
 // What a scan needs to know about the draw.
@@ -795,7 +820,7 @@ struct DrawParams {
 // so their weight is 0 or NaN and their key +inf.
 template <int DT, bool RESIDUAL>
 __device__ __forceinline__ void score_vec(const RawVec<DT>& rt, const RawVec<DT>& rd, int64_t vi,
-                                          const DrawParams& dp, Top2& best) {
+                                          const DrawParams& dp, Best2& best) {
   const uint32_t c0 = uint32_t(vi * 2);
   const Philox4 lo = philox4x32_10(c0, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
   const Philox4 hi = philox4x32_10(c0 + 1u, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
@@ -808,8 +833,9 @@ __device__ __forceinline__ void score_vec(const RawVec<DT>& rt, const RawVec<DT>
     if constexpr (RESIDUAL) w -= __builtin_amdgcn_exp2f(a2 + fmaf(zd - zt, dp.k2, dp.D2));
     const uint32_t word = t < 4 ? lo.w[t] : hi.w[t - 4];
     const float e2 = -__builtin_amdgcn_logf(unit_uniform(word));
-    const float key = w > 0.0f ? e2 * __builtin_amdgcn_rcpf(w) : INFINITY;
-    top2_push(best, key, int32_t(vi * kVec + t), zt, zd);
+    // w <= 0 (and NaN, from -inf logits) give +inf: rcp(+0) = +inf and e2 > 0
+    const float key = e2 * __builtin_amdgcn_rcpf(fmaxf(w, 0.0f));
+    best2_push(best, cand_pack(key, int32_t(vi * kVec + t)));
   }
 }
 
@@ -823,7 +849,7 @@ __device__ __forceinline__ void score_vec(const RawVec<DT>& rt, const RawVec<DT>
 template <int DT, bool RESIDUAL>
 __device__ __forceinline__ void score_vec_filtered(const RawVec<DT>& rt, const RawVec<DT>& rd,
                                                    int64_t vi, const DrawParams& dp, float thr,
-                                                   Top2& best) {
+                                                   Best2& best) {
   const uint32_t c0 = uint32_t(vi * 2);
   const Philox4 lo = philox4x32_10(c0, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
   const Philox4 hi = philox4x32_10(c0 + 1u, dp.pos, dp.r, kPurposeSample, dp.s0, dp.s1);
@@ -842,8 +868,8 @@ __device__ __forceinline__ void score_vec_filtered(const RawVec<DT>& rt, const R
         float w = p;
         if constexpr (RESIDUAL) w -= __builtin_amdgcn_exp2f(a2 + fmaf(zd - zt, dp.k2, dp.D2));
         const float e2 = -__builtin_amdgcn_logf(u);
-        const float key = w > 0.0f ? e2 * __builtin_amdgcn_rcpf(w) : INFINITY;
-        top2_push(best, key, int32_t(vi * kVec + t), zt, zd);
+        const float key = e2 * __builtin_amdgcn_rcpf(fmaxf(w, 0.0f));
+        best2_push(best, cand_pack(key, int32_t(vi * kVec + t)));
       }
     }
   }
@@ -904,7 +930,7 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
 // of several rounds) and costs latency where a single round of workgroups is
 // bound by its dependent steps.
 template <int DT, bool VEC, bool RESIDUAL, bool FILTER, int SI>
-__device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d, int64_t split,
+__device__ __forceinline__ Best2 scan_split(const void* row_t, const void* row_d, int64_t split,
                                            int64_t V, const DrawParams& dp) {
   constexpr int64_t kSplitVecs = int64_t(kBlock) * SI;  // vectors per split
   const int64_t vpr = (V + kVec - 1) / kVec;
@@ -920,7 +946,7 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
       wt[it] = load_vec<DT, true>(row_t, vc);
       if constexpr (RESIDUAL) wd[it] = load_vec<DT, true>(row_d, vc);
     }
-    Top2 best = top2_empty();
+    Best2 best = best2_empty();
     if constexpr (FILTER) {
       float thr = INFINITY;  // two keys of one lane are at most thr
 #pragma unroll
@@ -928,7 +954,7 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
         const int64_t vi = vi0 + int64_t(kWave) * it;
         if (vi < vpr)
           score_vec_filtered<DT, RESIDUAL>(wt[it], RESIDUAL ? wd[it] : wt[it], vi, dp, thr, best);
-        float m = best.k2;
+        float m = cand_key(best.c2);
 #pragma unroll
         for (int off = kWave / 2; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off, kWave));
         thr = m;
@@ -950,7 +976,7 @@ __device__ __forceinline__ Top2 scan_split(const void* row_t, const void* row_d,
     rt[it] = inside ? load_vec_bounded<DT, VEC>(row_t, vi, V) : neg_inf_vec<DT>();
     rd[it] = inside && RESIDUAL ? load_vec_bounded<DT, VEC>(row_d, vi, V) : rt[it];
   }
-  Top2 best = top2_empty();
+  Best2 best = best2_empty();
 #pragma unroll 1
   for (int it = 0; it < SI; ++it) {
     const int64_t vi = vi0 + int64_t(kWave) * it;
@@ -974,13 +1000,13 @@ __device__ __forceinline__ int32_t draw_from_p(const void* row_t, int64_t V, dou
   const int lane = threadIdx.x & (kWave - 1);
   dp.D2 = 0.0f;
   const int64_t vpr = (V + kVec - 1) / kVec;
-  Top2 fb = top2_empty();
+  Best2 fb = best2_empty();
   for (int64_t vi = lane; vi < vpr; vi += kWave) {
     const RawVec<DT> pt = load_vec_bounded<DT, VEC>(row_t, vi, V);
     score_vec<DT, false>(pt, pt, vi, dp, fb);
   }
-  fb = wave_top2(fb);
-  const int32_t id = rescore_top2(fb, false, T, lzt, 0.0, dp.pos, dp.r, dp.s0, dp.s1).id;
+  const Top2 all = with_logits<DT>(wave_best2(fb), row_t, row_t, false, V);
+  const int32_t id = rescore_top2(all, false, T, lzt, 0.0, dp.pos, dp.r, dp.s0, dp.s1).id;
   return __shfl(id, 0, kWave);
 }
 
@@ -1255,10 +1281,11 @@ void draw_kernel(ChainArgs a) {
   dp.s1 = uint32_t(a.seed >> 32);
   // the fused kernel runs one round of workgroups (latency-bound); the
   // separate-accept path serves grids of several rounds
-  Top2 best = residual ? scan_split<DT, VEC, true, !FUSED, SI>(row_t, row_d, split, a.V, dp)
-                       : scan_split<DT, VEC, false, !FUSED, SI>(row_t, row_d, split, a.V, dp);
-  best = wave_top2(best);
-  if (lane == 0) s_top[t / kWave] = best;
+  const Best2 best = residual ? scan_split<DT, VEC, true, !FUSED, SI>(row_t, row_d, split, a.V, dp)
+                              : scan_split<DT, VEC, false, !FUSED, SI>(row_t, row_d, split, a.V, dp);
+  // the logit loads of the wavefront's best two overlap the wait for the others
+  const Top2 wbest = with_logits<DT>(wave_best2(best), row_t, row_d, residual, a.V);
+  if (lane == 0) s_top[t / kWave] = wbest;
   __syncthreads();
   if (t < kWave) {
     Top2 all = s_top[0];
