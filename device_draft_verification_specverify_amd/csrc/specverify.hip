@@ -1093,18 +1093,33 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
   const bool sampled = T > 0.0f;
   const bool greedy = T == 0.0f;
   const double k2 = double(kLog2e / T);
-  int32_t x = 0;
-  bool tok_bad = false;
-  if (t < G) {
-    x = a.tokens[chain * G + t];
-    tok_bad = x < 0 || int64_t(x) >= a.V;
+  // The draft tokens, the logits at them and the accept uniforms go through
+  // the last wavefront, whose loads then wait on nothing of the partials' (it
+  // folds rows only when a chain has more than 24 rows); LDS hands them over.
+  __shared__ int32_t s_tok[SV_MAX_GAMMA];
+  __shared__ float s_zt[SV_MAX_GAMMA], s_zd[SV_MAX_GAMMA];
+  __shared__ double s_logu[SV_MAX_GAMMA];
+  constexpr int kTokWave = (kBlock / kWave - 1) * kWave;
+  if (t >= kTokWave && t - kTokWave < G) {
+    const int j = t - kTokWave;
+    const int32_t x = a.tokens[chain * G + j];
+    float zt = 0.0f, zd = 0.0f;
+    if (!(x < 0 || int64_t(x) >= a.V) && sampled) {
+      zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj), x);
+      zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj), x);
+    }
+    const uint64_t pos = uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(j);
+    const Philox4 r = philox4x32_10(0u, uint32_t(pos), uint32_t(chain), kPurposeAccept,
+                                    uint32_t(a.seed), uint32_t(a.seed >> 32));
+    s_tok[j] = x;
+    s_zt[j] = zt;
+    s_zd[j] = zd;
+    s_logu[j] = log_uniform_d(unit_uniform_d(r.w[0]));
   }
   const int grp = t / kRowLanes;
   const int gl = t % kRowLanes;
   const int nr = P + (sampled ? G : 0);
   int32_t bad = 0;
-  float zt = 0.0f, zd = 0.0f;
-  double log_u = 0.0;
   for (int base = 0; base < nr; base += kRowsPerPass) {
     const int ri = base + grp;
     const bool has = ri < nr;
@@ -1121,17 +1136,6 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) fold_partial(m, idx, s, q[u], sampled, k2);
-    }
-    if (base == 0 && t < G) {
-      // the logits at the draft tokens and the accept uniforms, while the rows reduce
-      if (!tok_bad && sampled) {
-        zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + t * rs.tsj), x);
-        zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + t * rs.dsj), x);
-      }
-      const uint64_t pos = uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(t);
-      const Philox4 r = philox4x32_10(0u, uint32_t(pos), uint32_t(chain), kPurposeAccept,
-                                      uint32_t(a.seed), uint32_t(a.seed >> 32));
-      log_u = log_uniform_d(unit_uniform_d(r.w[0]));
     }
     // combine the 8 lanes of each row in a fixed order
     float M = m;
@@ -1162,14 +1166,17 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
   // accept tests of the G positions in wavefront 0, first rejection by ballot
   if (t < kWave) {
     bool acc = false;
+    bool tok_bad = false;
     if (t < G) {
       const int j = t;
+      const int32_t x = s_tok[j];
+      tok_bad = x < 0 || int64_t(x) >= a.V;
       double lp = 0.0, lq = 0.0;
       if (!tok_bad) {
         if (sampled) {
-          lp = double(zt) / double(T) - s_lnz[j];
-          lq = double(zd) / double(T) - s_lnz[P + j];
-          acc = log_u < lp - lq;
+          lp = double(s_zt[j]) / double(T) - s_lnz[j];
+          lq = double(s_zd[j]) / double(T) - s_lnz[P + j];
+          acc = s_logu[j] < lp - lq;
         } else if (greedy) {
           acc = x == s_amax[j];
           lp = acc ? 0.0 : -INFINITY;
