@@ -100,6 +100,15 @@ struct alignas(16) Cand {
   int32_t pad;
 };
 
+// What the accept test needs of one draft position of one chain, gathered
+// during the stream by its grid's last workgroup: the target and draft logits
+// at the draft token (0 for greedy rows and invalid tokens) and ln u of the
+// accept uniform.
+struct alignas(16) TokenAux {
+  float zt, zd;
+  double log_u;
+};
+
 // What the draw and finish kernels need of a chain (written by split 0 of the
 // step's draw kernel, or by given_kernel).
 struct alignas(16) ChainInfo {
@@ -153,6 +162,16 @@ __device__ __forceinline__ double unit_uniform_d(uint32_t w) {
 // ln u in double; for u >= 1/2, u - 1 is exact and log1p keeps full accuracy.
 __device__ __forceinline__ double log_uniform_d(double u) {
   return u >= 0.5 ? log1p(u - 1.0) : log(u);
+}
+
+// ln u of the accept test's uniform of chain r at draft position j: Philox
+// counter (0, pos0[b] + j, r, accept purpose), first word.
+__device__ __forceinline__ double accept_log_u(uint64_t seed, const int64_t* pos0, int64_t b,
+                                               int64_t j, int64_t r) {
+  const uint64_t pos = uint64_t(pos0 ? pos0[b] : 0) + uint64_t(j);
+  const Philox4 w = philox4x32_10(0u, uint32_t(pos), uint32_t(r), kPurposeAccept, uint32_t(seed),
+                                  uint32_t(seed >> 32));
+  return log_uniform_d(unit_uniform_d(w.w[0]));
 }
 
 // ---------------------------------------------------------------------------
@@ -497,10 +516,41 @@ struct StreamArgs {
   int32_t* rank_out;     // [B + 1]: sampled batch rows before b; [B] = their total
   uint32_t* clear;       // [nclear] per-chain counters the next launch counts on, zeroed here
   int64_t nclear;
+  // The step: one more workgroup than the stream needs gathers tok_aux [B*K*G]
+  // (gather_tokens) instead of streaming; null otherwise.
+  TokenAux* tok_aux;
+  const int32_t* tokens;  // [B, K, G]
+  const int64_t* pos0;
+  uint64_t seed;
   // The chunk-index divisions (by cpr, P, K*G, G) as multiply-shifts: every
   // chunk index is below 2^31 (the host rejects larger calls).
   FastDiv by_cpr, by_p, by_kg, by_g;
 };
+
+// The step's token gather (the stream grid's extra, last workgroup): for every
+// (chain, position) the logits at the draft token, read only for sampled rows
+// and valid tokens, and ln u of the accept uniform (Philox counter (0,
+// position, chain, accept purpose)), so that the draws' prologue finds them
+// with one load that depends on nothing. With one workgroup per CU this
+// workgroup starts when the first streaming one ends.
+template <int DT>
+__device__ void gather_tokens(const StreamArgs& a) {
+  constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  const RowSet& rs = a.rs;
+  for (int64_t i = threadIdx.x; i < rs.B * rs.K * rs.G; i += kStreamBlock) {
+    const int64_t chain = int64_t(fast_div(uint32_t(i), a.by_g));
+    const int64_t j = i - chain * rs.G;
+    const int64_t b = int64_t(uint32_t(chain) / uint32_t(rs.K));
+    const int64_t k = chain - b * rs.K;
+    const int32_t x = a.tokens[i];
+    float zt = 0.0f, zd = 0.0f;
+    if (!(x < 0 || int64_t(x) >= a.V) && rs.temp[b] > 0.0f) {
+      zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj), x);
+      zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj), x);
+    }
+    a.tok_aux[i] = TokenAux{zt, zd, accept_log_u(a.seed, a.pos0, b, j, chain)};
+  }
+}
 
 // Persistent workgroups (one per CU) walk the chunks of the flattened stream
 // round robin (workgroup g owns chunks g, g + G, g + 2G, ...; its wavefronts
@@ -519,9 +569,14 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
   const int64_t KG = rs.K * rs.G;
   const int nchunks = int((rs.B + 63) / 64);
   int64_t nrows = a.nrows;
+  const int64_t nblk = int64_t(gridDim.x) - (a.tok_aux ? 1 : 0);  // streaming workgroups
+  if (a.tok_aux && int64_t(blockIdx.x) == nblk) {
+    gather_tokens<DT>(a);
+    return;
+  }
   if (threadIdx.x == 0) s_claim = 0u;
   for (int64_t i = int64_t(blockIdx.x) * kStreamBlock + threadIdx.x; i < a.nclear;
-       i += int64_t(gridDim.x) * kStreamBlock)
+       i += nblk * kStreamBlock)
     a.clear[i] = 0u;
   __syncthreads();
   if (a.compact) {
@@ -537,7 +592,6 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
   }
   const int64_t cv = int64_t(kWave) * CL;
   const int64_t total = nrows * a.cpr;
-  const int64_t nblk = gridDim.x;
   const bool v_tail = (a.V % kVec) != 0;
   // workgroup g owns chunks g, g + nblk, ...; its wavefronts claim them in order
   uint32_t claim = 0;
@@ -699,12 +753,6 @@ __device__ __forceinline__ void pub64(void* p, uint64_t v) {
 __device__ __forceinline__ uint64_t get64(const void* p) {
   return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void pub32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t get32(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t bump32(uint32_t* p) {
   return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1016,6 +1064,7 @@ struct ChainArgs {
   const RowPartial* part;    // stream chunk partials by batch-row slot
   int64_t cpr;               // chunks per row
   const int32_t* tokens;     // [B, K, G]
+  const TokenAux* tok_aux;   // [B, K, G], from the stream kernel's token gather
   uint64_t seed;
   const int64_t* pos0;
   // outputs (split 0 of the draw kernel's chain; out_token of a sampled chain: its last split)
@@ -1093,9 +1142,11 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
   const bool sampled = T > 0.0f;
   const bool greedy = T == 0.0f;
   const double k2 = double(kLog2e / T);
-  // The draft tokens, the logits at them and the accept uniforms go through
-  // the last wavefront, whose loads then wait on nothing of the partials' (it
-  // folds rows only when a chain has more than 24 rows); LDS hands them over.
+  // The draft tokens, the logits at them and the accept uniforms (gathered by
+  // the stream kernel when tok_aux is set, else loaded and drawn here) go
+  // through the last wavefront, whose loads then wait on nothing of the
+  // partials' (it folds rows only when a chain has more than 24 rows); LDS
+  // hands them over.
   __shared__ int32_t s_tok[SV_MAX_GAMMA];
   __shared__ float s_zt[SV_MAX_GAMMA], s_zd[SV_MAX_GAMMA];
   __shared__ double s_logu[SV_MAX_GAMMA];
@@ -1103,18 +1154,20 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
   if (t >= kTokWave && t - kTokWave < G) {
     const int j = t - kTokWave;
     const int32_t x = a.tokens[chain * G + j];
-    float zt = 0.0f, zd = 0.0f;
-    if (!(x < 0 || int64_t(x) >= a.V) && sampled) {
-      zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj), x);
-      zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj), x);
+    TokenAux q{0.0f, 0.0f, 0.0};
+    if (a.tok_aux) {
+      q = a.tok_aux[chain * G + j];
+    } else {
+      if (!(x < 0 || int64_t(x) >= a.V) && sampled) {
+        q.zt = load_one<DT>(row_ptr(rs.t, esz, b * rs.tsb + j * rs.tsj), x);
+        q.zd = load_one<DT>(row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + j * rs.dsj), x);
+      }
+      q.log_u = accept_log_u(a.seed, a.pos0, b, j, chain);
     }
-    const uint64_t pos = uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(j);
-    const Philox4 r = philox4x32_10(0u, uint32_t(pos), uint32_t(chain), kPurposeAccept,
-                                    uint32_t(a.seed), uint32_t(a.seed >> 32));
     s_tok[j] = x;
-    s_zt[j] = zt;
-    s_zd[j] = zd;
-    s_logu[j] = log_uniform_d(unit_uniform_d(r.w[0]));
+    s_zt[j] = q.zt;
+    s_zd[j] = q.zd;
+    s_logu[j] = q.log_u;
   }
   const int grp = t / kRowLanes;
   const int gl = t % kRowLanes;
@@ -2087,7 +2140,7 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   int64_t vpr, cpr, nrows, chains, nsplit;
-  size_t off_part, off_rank, off_info, off_top, total;
+  size_t off_part, off_rank, off_info, off_top, off_tok, total;
 };
 
 // Chain counters at the start of every workspace. The first launch of every
@@ -2099,7 +2152,8 @@ constexpr int64_t kMaxCountedChains = 65536;
 constexpr size_t kCounterBytes = kMaxCountedChains * sizeof(uint32_t);
 
 // One chunk partial per (stream row, chunk); every row of the batch counted.
-Layout make_layout(int64_t B, int64_t nrows, int64_t chains, int64_t V, int dtype) {
+Layout make_layout(int64_t B, int64_t nrows, int64_t chains, int64_t V, int dtype,
+                   int64_t ntok = 0) {
   Layout L;
   L.vpr = (V + kVec - 1) / kVec;
   const int64_t cv = chunk_vectors(dtype);
@@ -2111,7 +2165,8 @@ Layout make_layout(int64_t B, int64_t nrows, int64_t chains, int64_t V, int dtyp
   L.off_rank = align256(L.off_part + size_t(nrows) * size_t(L.cpr) * sizeof(RowPartial));
   L.off_info = align256(L.off_rank + size_t(B + 1) * sizeof(int32_t));
   L.off_top = align256(L.off_info + size_t(chains) * sizeof(ChainInfo));
-  L.total = align256(L.off_top + size_t(chains) * size_t(L.nsplit) * sizeof(Cand));
+  L.off_tok = align256(L.off_top + size_t(chains) * size_t(L.nsplit) * sizeof(Cand));
+  L.total = align256(L.off_tok + size_t(ntok) * sizeof(TokenAux));
   return L;
 }
 
@@ -2172,6 +2227,7 @@ void launch_stream_t(const StreamArgs& sa, hipStream_t st, hipEvent_t ev0, hipEv
   int64_t grid = stream_blocks<DT, VEC, ARGMAX_ALL>();
   const int64_t need = (sa.nrows * sa.cpr + kStreamWaves - 1) / kStreamWaves;
   if (grid > need) grid = need;
+  if (sa.tok_aux) grid += 1;  // the token gather
   if (ev0)
     hipExtLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(grid)),
                           dim3(kStreamBlock), 0, st, ev0, ev1, 0u, sa);
@@ -2322,7 +2378,7 @@ bool workspace_ok(void* ws, size_t have, size_t need, int* status) {
 bool stream_chunks_ok(const Layout& L) { return L.nrows * L.cpr < (int64_t(1) << 31); }
 
 Layout step_layout(int64_t B, int64_t K, int64_t G, int64_t V, int dtype) {
-  return make_layout(B, B * (G + 1) + B * K * G, B * K, V, dtype);
+  return make_layout(B, B * (G + 1) + B * K * G, B * K, V, dtype, B * K * G);
 }
 
 bool logits_vec_ok(const void* t, const void* d, int esz, int64_t tsb, int64_t tsj, int64_t dsb,
@@ -2639,6 +2695,17 @@ int step_launch(const void* target_logits, const void* draft_logits, int dtype,
   sa.rank_out = compact ? rank : nullptr;
   sa.clear = B * K <= kMaxCountedChains ? reinterpret_cast<uint32_t*>(base) : nullptr;
   sa.nclear = sa.clear ? B * K : 0;
+  // The token gather takes one workgroup of the stream's grid: with at most
+  // one (chain, position) per thread it ends well before the stream does (it
+  // starts when the first streaming workgroup ends); larger batches draw the
+  // accept uniforms in the draws' prologue instead (B=512 K=4 gamma=8: the
+  // gather's 16 rounds of scattered loads lengthened the stream by ~38 us).
+  TokenAux* tok_aux =
+      B * K * gamma <= kStreamBlock ? reinterpret_cast<TokenAux*>(base + L.off_tok) : nullptr;
+  sa.tok_aux = tok_aux;
+  sa.tokens = draft_tokens;
+  sa.pos0 = pos0;
+  sa.seed = seed;
   launch_stream(dtype, vec, false, sa, st);
 
   ChainArgs ca{};
@@ -2647,6 +2714,7 @@ int step_launch(const void* target_logits, const void* draft_logits, int dtype,
   ca.part = part;
   ca.cpr = L.cpr;
   ca.tokens = draft_tokens;
+  ca.tok_aux = tok_aux;
   ca.seed = seed;
   ca.pos0 = pos0;
   ca.accept_len = accept_len;
