@@ -201,8 +201,11 @@ def sample_tokens(target, draft, T, lnz_t, lnz_d, argmax_t, n, seed: int, pos0, 
     if res.any():
         b, k, nn = bb[res], kk[res], n[res]
         Tc = T[b][:, None]
-        lp = scaled_logits(target[b, target_row_for(nn)], Tc) - lnz_t[b, target_row_for(nn)][:, None]
-        lq = scaled_logits(draft[b, k, nn], Tc) - lnz_d[b, k, nn][:, None]
+        # a row whose maximum is not finite gives NaN here; such rows are
+        # input errors (verify sets their chains' outputs to -1)
+        with np.errstate(invalid="ignore"):
+            lp = scaled_logits(target[b, target_row_for(nn)], Tc) - lnz_t[b, target_row_for(nn)][:, None]
+            lq = scaled_logits(draft[b, k, nn], Tc) - lnz_d[b, k, nn][:, None]
         logr = residual_log_weights(lp, lq)
         G = sampling_noise(seed, chain_rows[res], pos0[b] + nn, V)
         no_support = np.all(np.isneginf(logr), axis=-1)
