@@ -824,15 +824,69 @@ __device__ __forceinline__ void best2_push(Best2& s, double c) {
   s.c1 = fmin(s.c1, c);
 }
 
+// Lane moves inside rows of 16 lanes by DPP (a VALU operand modifier, no
+// LDS round trip): quad_perm [1,0,3,2] and [2,3,0,1] (lane ^ 1, lane ^ 2),
+// row_half_mirror (i <-> 7 - i within 8 lanes) and row_mirror (i <-> 15 - i
+// within 16). Applied in that order, each pairs lanes whose partial results
+// cover disjoint groups, so after the four every lane of a row holds its
+// row's result (for order-free operations such as min and max).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double x) {
+  const uint64_t b = uint64_t(__double_as_longlong(x));
+  const uint64_t lo = dpp32<CTRL>(uint32_t(b)), hi = dpp32<CTRL>(uint32_t(b >> 32));
+  return __longlong_as_double(int64_t((hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane64(double x, int l) {
+  const uint64_t b = uint64_t(__double_as_longlong(x));
+  const uint64_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), l));
+  const uint64_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), l));
+  return __longlong_as_double(int64_t((hi << 32) | lo));
+}
+
+__device__ __forceinline__ void best2_merge(Best2& v, double o1, double o2) {
+  v.c2 = fmin(fmax(v.c1, o1), fmin(v.c2, o2));
+  v.c1 = fmin(v.c1, o1);
+}
+
+// The wavefront's best two in every lane: DPP inside each row of 16 lanes,
+// then the four rows' results read from lanes 0, 16, 32 and 48.
 __device__ __forceinline__ Best2 wave_best2(Best2 v) {
+  best2_merge(v, dpp64<kDppXor1>(v.c1), dpp64<kDppXor1>(v.c2));
+  best2_merge(v, dpp64<kDppXor2>(v.c1), dpp64<kDppXor2>(v.c2));
+  best2_merge(v, dpp64<kDppHalfMirror>(v.c1), dpp64<kDppHalfMirror>(v.c2));
+  best2_merge(v, dpp64<kDppMirror>(v.c1), dpp64<kDppMirror>(v.c2));
+  Best2 w{readlane64(v.c1, 0), readlane64(v.c2, 0)};
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const double o1 = __shfl_xor(v.c1, off, kWave);
-    const double o2 = __shfl_xor(v.c2, off, kWave);
-    v.c2 = fmin(fmax(v.c1, o1), fmin(v.c2, o2));
-    v.c1 = fmin(v.c1, o1);
+  for (int r = 1; r < kWave / 16; ++r) best2_merge(w, readlane64(v.c1, 16 * r), readlane64(v.c2, 16 * r));
+  return w;
+}
+
+// The wavefront's best (float64 score, id) in every lane: the highest score,
+// ties to the lowest id (order-free, so DPP inside rows, then the rows).
+__device__ __forceinline__ void cand_better(double& bs, int32_t& id, double ob, int32_t oi) {
+  if (ob > bs || (ob == bs && oi < id)) {
+    bs = ob;
+    id = oi;
   }
-  return v;
+}
+__device__ __forceinline__ void wave_best_cand(double& bs, int32_t& id) {
+  cand_better(bs, id, dpp64<kDppXor1>(bs), int32_t(dpp32<kDppXor1>(uint32_t(id))));
+  cand_better(bs, id, dpp64<kDppXor2>(bs), int32_t(dpp32<kDppXor2>(uint32_t(id))));
+  cand_better(bs, id, dpp64<kDppHalfMirror>(bs), int32_t(dpp32<kDppHalfMirror>(uint32_t(id))));
+  cand_better(bs, id, dpp64<kDppMirror>(bs), int32_t(dpp32<kDppMirror>(uint32_t(id))));
+  double wb = readlane64(bs, 0);
+  int32_t wi = __builtin_amdgcn_readlane(id, 0);
+#pragma unroll
+  for (int r = 1; r < kWave / 16; ++r)
+    cand_better(wb, wi, readlane64(bs, 16 * r), __builtin_amdgcn_readlane(id, 16 * r));
+  bs = wb;
+  id = wi;
 }
 
 // The wavefront's best two (every lane holds them) with their target and draft
@@ -1377,15 +1431,7 @@ void draw_kernel(ChainArgs a) {
       id = q.id;
     }
   }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const double ob = __shfl_xor(bs, off, kWave);
-    const int32_t oi = __shfl_xor(id, off, kWave);
-    if (ob > bs || (ob == bs && oi < id)) {
-      bs = ob;
-      id = oi;
-    }
-  }
+  wave_best_cand(bs, id);
   if (id == INT_MAX) id = draw_from_p<DT, VEC>(row_t, a.V, double(T), lzt, dp);
   if (lane == 0) a.out_token[chain] = id == INT_MAX ? -1 : id;
 }
@@ -1418,15 +1464,7 @@ __global__ __launch_bounds__(kWave) void finish_kernel(const void* tgt, int64_t 
       id = c.id;
     }
   }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const double ob = __shfl_xor(best, off, kWave);
-    const int32_t oi = __shfl_xor(id, off, kWave);
-    if (ob > best || (ob == best && oi < id)) {
-      best = ob;
-      id = oi;
-    }
-  }
+  wave_best_cand(best, id);
   if (id == INT_MAX) {
     const int64_t b = chain / K;
     const float T = temp[b];
