@@ -310,6 +310,49 @@ __device__ __forceinline__ void better_max(float& m, int32_t& i, float om, int32
   }
 }
 
+// Lane moves inside rows of 16 lanes by DPP (a VALU operand modifier, no
+// LDS round trip): quad_perm [1,0,3,2] and [2,3,0,1] (lane ^ 1, lane ^ 2),
+// row_half_mirror (i <-> 7 - i within 8 lanes) and row_mirror (i <-> 15 - i
+// within 16). Applied in that order, each pairs lanes whose partial results
+// cover disjoint groups, so after the four every lane of a row holds its
+// row's result (for order-free operations such as min and max).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double x) {
+  const uint64_t b = uint64_t(__double_as_longlong(x));
+  const uint64_t lo = dpp32<CTRL>(uint32_t(b)), hi = dpp32<CTRL>(uint32_t(b >> 32));
+  return __longlong_as_double(int64_t((hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane64(double x, int l) {
+  const uint64_t b = uint64_t(__double_as_longlong(x));
+  const uint64_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), l));
+  const uint64_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), l));
+  return __longlong_as_double(int64_t((hi << 32) | lo));
+}
+
+// A row's 8 lanes (kRowLanes) combined by DPP: lane ^ 1, lane ^ 2, then the
+// two quads (row_half_mirror); every lane of the 8 gets the result. The
+// argmax is order-free; the sum's order is fixed, and the draws' prologue
+// and finalize_rows_kernel both use it, so a row gets the same bits from
+// either.
+__device__ __forceinline__ void group8_argmax(float& m, int32_t& i) {
+  better_max(m, i, __uint_as_float(dpp32<kDppXor1>(__float_as_uint(m))), int32_t(dpp32<kDppXor1>(uint32_t(i))));
+  better_max(m, i, __uint_as_float(dpp32<kDppXor2>(__float_as_uint(m))), int32_t(dpp32<kDppXor2>(uint32_t(i))));
+  better_max(m, i, __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(m))),
+             int32_t(dpp32<kDppHalfMirror>(uint32_t(i))));
+}
+__device__ __forceinline__ double group8_sum(double x) {
+  x += dpp64<kDppXor1>(x);
+  x += dpp64<kDppXor2>(x);
+  x += dpp64<kDppHalfMirror>(x);
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // Rows and their place in the flattened stream. Target rows come first, in
 // (b, j) order; then the K*G draft rows of every batch row that needs them, in
@@ -382,7 +425,7 @@ __device__ __forceinline__ double row_lnz(float M, double sr, float T) {
 // Statistics of one stream row by a group of kRowLanes consecutive lanes, for
 // rows of few chunks: lane gl of the group folds chunks gl, gl + 8, ..., four
 // loads in flight at a time (has == false: the lane folds nothing), and
-// group_reduce_row combines the group in a fixed order (xor 4, 2, 1). The
+// group_reduce_row combines the group in a fixed order (group8_sum). The
 // draws' prologue folds and combines its rows in this same order, inline, so
 // that both give a row the same bits. Every lane of the wavefront calls
 // group_reduce_row; all lanes of a group get the result (lnZ as row_lnz).
@@ -411,15 +454,9 @@ __device__ __forceinline__ RowStat group_reduce_row(float m, int32_t idx, double
   const double k2 = double(kLog2e / T);
   float M = m;
   int32_t I = idx;
-#pragma unroll
-  for (int off = kRowLanes / 2; off > 0; off >>= 1) {
-    const float om = __shfl_xor(M, off, kWave);
-    const int32_t oi = __shfl_xor(I, off, kWave);
-    better_max(M, I, om, oi);
-  }
+  group8_argmax(M, I);
   double sr = (sampled && M > -INFINITY && m > -INFINITY) ? s * exp2_scale((double(m) - double(M)) * k2) : s;
-#pragma unroll
-  for (int off = kRowLanes / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
+  sr = group8_sum(sr);
   RowStat out;
   out.m = M;
   out.idx = I;
@@ -824,31 +861,6 @@ __device__ __forceinline__ void best2_push(Best2& s, double c) {
   s.c1 = fmin(s.c1, c);
 }
 
-// Lane moves inside rows of 16 lanes by DPP (a VALU operand modifier, no
-// LDS round trip): quad_perm [1,0,3,2] and [2,3,0,1] (lane ^ 1, lane ^ 2),
-// row_half_mirror (i <-> 7 - i within 8 lanes) and row_mirror (i <-> 15 - i
-// within 16). Applied in that order, each pairs lanes whose partial results
-// cover disjoint groups, so after the four every lane of a row holds its
-// row's result (for order-free operations such as min and max).
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
-  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ double dpp64(double x) {
-  const uint64_t b = uint64_t(__double_as_longlong(x));
-  const uint64_t lo = dpp32<CTRL>(uint32_t(b)), hi = dpp32<CTRL>(uint32_t(b >> 32));
-  return __longlong_as_double(int64_t((hi << 32) | lo));
-}
-__device__ __forceinline__ double readlane64(double x, int l) {
-  const uint64_t b = uint64_t(__double_as_longlong(x));
-  const uint64_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), l));
-  const uint64_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), l));
-  return __longlong_as_double(int64_t((hi << 32) | lo));
-}
-
 __device__ __forceinline__ void best2_merge(Best2& v, double o1, double o2) {
   v.c2 = fmin(fmax(v.c1, o1), fmin(v.c2, o2));
   v.c1 = fmin(v.c1, o1);
@@ -1247,15 +1259,9 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
     // combine the 8 lanes of each row in a fixed order
     float M = m;
     int32_t I = idx;
-#pragma unroll
-    for (int off = kRowLanes / 2; off > 0; off >>= 1) {
-      const float om = __shfl_xor(M, off, kWave);
-      const int32_t oi = __shfl_xor(I, off, kWave);
-      better_max(M, I, om, oi);
-    }
+    group8_argmax(M, I);
     double sr = (sampled && M > -INFINITY && m > -INFINITY) ? s * exp2_scale((double(m) - double(M)) * k2) : s;
-#pragma unroll
-    for (int off = kRowLanes / 2; off > 0; off >>= 1) sr += __shfl_xor(sr, off, kWave);
+    sr = group8_sum(sr);
     if (has && gl == 0) {
       const double lnz = row_lnz(M, sr, T);
       s_lnz[ri] = lnz;
