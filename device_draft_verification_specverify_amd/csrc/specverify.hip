@@ -346,6 +346,18 @@ __device__ __forceinline__ void group8_argmax(float& m, int32_t& i) {
   better_max(m, i, __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(m))),
              int32_t(dpp32<kDppHalfMirror>(uint32_t(i))));
 }
+// The wavefront's minimum in every lane (DPP inside rows, then the rows).
+__device__ __forceinline__ float wave_min(float x) {
+  x = fminf(x, __uint_as_float(dpp32<kDppXor1>(__float_as_uint(x))));
+  x = fminf(x, __uint_as_float(dpp32<kDppXor2>(__float_as_uint(x))));
+  x = fminf(x, __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(x))));
+  x = fminf(x, __uint_as_float(dpp32<kDppMirror>(__float_as_uint(x))));
+  float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+#pragma unroll
+  for (int r = 1; r < kWave / 16; ++r)
+    w = fminf(w, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * r)));
+  return w;
+}
 __device__ __forceinline__ double group8_sum(double x) {
   x += dpp64<kDppXor1>(x);
   x += dpp64<kDppXor2>(x);
@@ -1068,10 +1080,7 @@ __device__ __forceinline__ Best2 scan_split(const void* row_t, const void* row_d
         const int64_t vi = vi0 + int64_t(kWave) * it;
         if (vi < vpr)
           score_vec_filtered<DT, RESIDUAL>(wt[it], RESIDUAL ? wd[it] : wt[it], vi, dp, thr, best);
-        float m = cand_key(best.c2);
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) m = fminf(m, __shfl_xor(m, off, kWave));
-        thr = m;
+        thr = wave_min(cand_key(best.c2));
       }
     } else {
 #pragma unroll
