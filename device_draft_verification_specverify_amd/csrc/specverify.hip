@@ -358,6 +358,33 @@ __device__ __forceinline__ float wave_min(float x) {
     w = fminf(w, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16 * r)));
   return w;
 }
+// The wavefront's sum in every lane, rows added in a fixed order.
+__device__ __forceinline__ double wave_sum(double x) {
+  x += dpp64<kDppXor1>(x);
+  x += dpp64<kDppXor2>(x);
+  x += dpp64<kDppHalfMirror>(x);
+  x += dpp64<kDppMirror>(x);
+  double w = readlane64(x, 0);
+#pragma unroll
+  for (int r = 1; r < kWave / 16; ++r) w += readlane64(x, 16 * r);
+  return w;
+}
+// The wavefront's largest value and its lowest id (better_max), in every lane.
+__device__ __forceinline__ void wave_argmax(float& m, int32_t& i) {
+  better_max(m, i, __uint_as_float(dpp32<kDppXor1>(__float_as_uint(m))), int32_t(dpp32<kDppXor1>(uint32_t(i))));
+  better_max(m, i, __uint_as_float(dpp32<kDppXor2>(__float_as_uint(m))), int32_t(dpp32<kDppXor2>(uint32_t(i))));
+  better_max(m, i, __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(m))),
+             int32_t(dpp32<kDppHalfMirror>(uint32_t(i))));
+  better_max(m, i, __uint_as_float(dpp32<kDppMirror>(__float_as_uint(m))), int32_t(dpp32<kDppMirror>(uint32_t(i))));
+  float wm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
+  int32_t wi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < kWave / 16; ++r)
+    better_max(wm, wi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16 * r)),
+               __builtin_amdgcn_readlane(i, 16 * r));
+  m = wm;
+  i = wi;
+}
 __device__ __forceinline__ double group8_sum(double x) {
   x += dpp64<kDppXor1>(x);
   x += dpp64<kDppXor2>(x);
@@ -1742,16 +1769,9 @@ __global__ __launch_bounds__(kBlock) void alpha_law_kernel(const OverlapPartial*
 #pragma unroll
     for (int q = 0; q < kAlphaBatch; ++q) {
       if (j0 + q >= G) break;  // uniform
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        s[q] += __shfl_xor(s[q], off, kWave);
-        const float otm = __shfl_xor(tm[q], off, kWave);
-        const int32_t oti = __shfl_xor(ti[q], off, kWave);
-        const float odm = __shfl_xor(dm[q], off, kWave);
-        const int32_t odi = __shfl_xor(di[q], off, kWave);
-        better_max(tm[q], ti[q], otm, oti);
-        better_max(dm[q], di[q], odm, odi);
-      }
+      s[q] = wave_sum(s[q]);
+      wave_argmax(tm[q], ti[q]);
+      wave_argmax(dm[q], di[q]);
       const int64_t j = j0 + q;
       const double aj = sampled ? s[q] : greedy ? (ti[q] == di[q] ? 1.0 : 0.0) : double(NAN);
       if (lane == 0) {
