@@ -953,8 +953,9 @@ __device__ __forceinline__ Top2 with_logits(const Best2& b, const void* row_t, c
     zt = load_one<DT>(row_t, id);
     if (residual) zd = load_one<DT>(row_d, id);
   }
-  return Top2{cand_key(b.c1), cand_id(b.c1), __shfl(zt, 0, kWave), __shfl(zd, 0, kWave),
-              cand_key(b.c2), cand_id(b.c2), __shfl(zt, 1, kWave), __shfl(zd, 1, kWave)};
+  auto lane_f = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+  return Top2{cand_key(b.c1), cand_id(b.c1), lane_f(zt, 0), lane_f(zd, 0),
+              cand_key(b.c2), cand_id(b.c2), lane_f(zt, 1), lane_f(zd, 1)};
 }
 
 // What a scan needs to know about the draw.
@@ -1059,7 +1060,7 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
     sc = rescore(residual, first ? all.i1 : all.i2, first ? all.t1 : all.t2,
                  first ? all.d1 : all.d2, T, lzt, lzd, pos, r, s0, s1);
   }
-  const double sc2 = __shfl(sc, 1, kWave);
+  const double sc2 = readlane64(sc, 1);
   Cand c{sc, all.i1, 0};
   if (sc2 > sc || (sc2 == sc && all.i2 < all.i1)) c = Cand{sc2, all.i2, 0};
   if (c.score == -INFINITY) c.id = INT_MAX;
@@ -1157,7 +1158,7 @@ __device__ __forceinline__ int32_t draw_from_p(const void* row_t, int64_t V, dou
   }
   const Top2 all = with_logits<DT>(wave_best2(fb), row_t, row_t, false, V);
   const int32_t id = rescore_top2(all, false, T, lzt, 0.0, dp.pos, dp.r, dp.s0, dp.s1).id;
-  return __shfl(id, 0, kWave);
+  return __builtin_amdgcn_readlane(id, 0);
 }
 
 struct ChainArgs {
