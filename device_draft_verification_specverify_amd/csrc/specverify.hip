@@ -609,6 +609,18 @@ struct StreamArgs {
 // position, chain, accept purpose)), so that the draws' prologue finds them
 // with one load that depends on nothing. With one workgroup per CU this
 // workgroup starts when the first streaming one ends.
+// The chunk of a persistent workgroup's i-th claim: chunk nblk*i + ((g + (i
+// mod 32)) mod nblk) for workgroup g of nblk. Without the rotation a row's short
+// last chunk would fall on the same few workgroups every time (all of them when
+// nblk is a multiple of the chunks per row, e.g. 256 workgroups and 32 chunks),
+// which would then idle while the others stream. Chunks rise with i, so a
+// workgroup's first one past the end ends its loop.
+__device__ __forceinline__ int64_t claimed_chunk(uint32_t i, int64_t nblk) {
+  int64_t o = int64_t(blockIdx.x) + int64_t(nblk >= 32 ? (i & 31u) : 0u);
+  if (o >= nblk) o -= nblk;
+  return o + nblk * int64_t(i);
+}
+
 template <int DT>
 __device__ void gather_tokens(const StreamArgs& a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
@@ -669,10 +681,10 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
   const int64_t cv = int64_t(kWave) * CL;
   const int64_t total = nrows * a.cpr;
   const bool v_tail = (a.V % kVec) != 0;
-  // workgroup g owns chunks g, g + nblk, ...; its wavefronts claim them in order
+  // the workgroup's wavefronts claim its chunks in order
   uint32_t claim = 0;
   if (lane == 0) claim = atomicAdd(&s_claim, 1u);
-  int64_t c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(claim));
+  int64_t c = claimed_chunk(__builtin_amdgcn_readfirstlane(claim), nblk);
   while (c < total) {
     uint32_t next = 0;
     if (lane == 0) next = atomicAdd(&s_claim, 1u);  // the next claim, answered during the loads
@@ -784,7 +796,7 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
       }
     }
     if (lane == 0 && unit_ok) a.part[slot * a.cpr + (c - rho * a.cpr)] = out;
-    c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(next));
+    c = claimed_chunk(__builtin_amdgcn_readfirstlane(next), nblk);
   }
 }
 
@@ -1598,7 +1610,7 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   uint32_t claim = 0;
   if (lane == 0) claim = atomicAdd(&s_claim, 1u);
-  int64_t c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(claim));
+  int64_t c = claimed_chunk(__builtin_amdgcn_readfirstlane(claim), nblk);
   while (c < total) {
     uint32_t next = 0;
     if (lane == 0) next = atomicAdd(&s_claim, 1u);
@@ -1609,7 +1621,7 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
     const int64_t v0 = chunk * cv;
     const int64_t v1 = v0 + cv < a.vpr ? v0 + cv : a.vpr;
     if (!sv_ok(b < rs.B && j < G && chunk < a.cpr && v0 < v1)) {
-      c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(next));
+      c = claimed_chunk(__builtin_amdgcn_readfirstlane(next), nblk);
       continue;
     }
     const float T = rs.temp[b];
@@ -1721,7 +1733,7 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
       }
       if (lane == 0) a.part[(chain * G + j) * a.cpr + chunk] = out;
     }
-    c = int64_t(blockIdx.x) + nblk * int64_t(__builtin_amdgcn_readfirstlane(next));
+    c = claimed_chunk(__builtin_amdgcn_readfirstlane(next), nblk);
   }
 }
 
