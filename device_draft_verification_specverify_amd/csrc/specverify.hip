@@ -2224,6 +2224,14 @@ __global__ __launch_bounds__(kBlock) void branch_prune_kernel(const float* __res
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Steps whose draw grid is small take narrower splits (down to 2048 ids, one
+// vector per thread) while the grid stays within half the CUs: each scan is
+// then shorter, and a chain's latency is what such a step waits for. The
+// candidate region holds the narrow count where chains * ceil(V / 2048) <=
+// kNarrowMaxSplits.
+constexpr int64_t kNarrowSplit = int64_t(kBlock) * kVec;
+constexpr int64_t kNarrowMaxSplits = 1024;
+
 struct Layout {
   int64_t vpr, cpr, nrows, chains, nsplit;
   size_t off_part, off_rank, off_info, off_top, off_tok, total;
@@ -2251,7 +2259,9 @@ Layout make_layout(int64_t B, int64_t nrows, int64_t chains, int64_t V, int dtyp
   L.off_rank = align256(L.off_part + size_t(nrows) * size_t(L.cpr) * sizeof(RowPartial));
   L.off_info = align256(L.off_rank + size_t(B + 1) * sizeof(int32_t));
   L.off_top = align256(L.off_info + size_t(chains) * sizeof(ChainInfo));
-  L.off_tok = align256(L.off_top + size_t(chains) * size_t(L.nsplit) * sizeof(Cand));
+  const int64_t narrow = (V + kNarrowSplit - 1) / kNarrowSplit;
+  const int64_t slots = chains * narrow <= kNarrowMaxSplits ? narrow : L.nsplit;
+  L.off_tok = align256(L.off_top + size_t(chains) * size_t(slots) * sizeof(Cand));
   L.total = align256(L.off_tok + size_t(ntok) * sizeof(TokenAux));
   return L;
 }
@@ -2398,6 +2408,21 @@ void launch_chain_finish(ChainArgs ca, bool given, hipStream_t st) {
     ca.nsplit = (ca.V + 2 * kSplit - 1) / (2 * kSplit);  // at most the workspace's count
     ca.by_nsplit = make_fastdiv(uint32_t(ca.nsplit));
   }
+  // a fused grid of at most one split per two CUs: vectors per thread 4 -> 2 -> 1
+  // (B=1 K=1 gamma=4 V=32000: 15.7 vs 17.5 us per step; B=16 gamma=5: 18.9 vs
+  // 19.7; one split per CU measured slower at B=16)
+  int si = kSampleIters;
+  if (fused) {
+    const int64_t cap = std::min<int64_t>(device_cus() / 2, kNarrowMaxSplits / 2);
+    for (int s = kSampleIters / 2; s >= 1; s /= 2) {
+      const int64_t ids = int64_t(kBlock) * kVec * s;
+      const int64_t ns = (ca.V + ids - 1) / ids;
+      if (chains * ns > cap) break;
+      si = s;
+      ca.nsplit = ns;
+    }
+    ca.by_nsplit = make_fastdiv(uint32_t(ca.nsplit));
+  }
   const dim3 grid{unsigned(chains * ca.nsplit), 1u, 1u};
   auto draws = [&]() {
     if constexpr (DT == SV_BF16)
@@ -2414,7 +2439,12 @@ void launch_chain_finish(ChainArgs ca, bool given, hipStream_t st) {
     draws();
   } else if (fused) {
     // every split derives n itself: one launch fewer, one prologue per workgroup
-    hipLaunchKernelGGL((draw_kernel<DT, VEC, true, kSampleIters>), grid, dim3(kBlock), 0, st, ca);
+    if (si == 1)
+      hipLaunchKernelGGL((draw_kernel<DT, VEC, true, 1>), grid, dim3(kBlock), 0, st, ca);
+    else if (si == 2)
+      hipLaunchKernelGGL((draw_kernel<DT, VEC, true, 2>), grid, dim3(kBlock), 0, st, ca);
+    else
+      hipLaunchKernelGGL((draw_kernel<DT, VEC, true, kSampleIters>), grid, dim3(kBlock), 0, st, ca);
   } else {
     // more workgroups than fit at once: n per chain in its own launch
     hipLaunchKernelGGL((accept_kernel<DT>), dim3(unsigned(chains)), dim3(kBlock), 0, st, ca);
