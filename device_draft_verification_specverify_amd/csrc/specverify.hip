@@ -603,12 +603,6 @@ struct StreamArgs {
   FastDiv by_cpr, by_p, by_kg, by_g;
 };
 
-// The step's token gather (the stream grid's extra, last workgroup): for every
-// (chain, position) the logits at the draft token, read only for sampled rows
-// and valid tokens, and ln u of the accept uniform (Philox counter (0,
-// position, chain, accept purpose)), so that the draws' prologue finds them
-// with one load that depends on nothing. With one workgroup per CU this
-// workgroup starts when the first streaming one ends.
 // The chunk of a persistent workgroup's i-th claim: chunk nblk*i + ((g + (i
 // mod 32)) mod nblk) for workgroup g of nblk. Without the rotation a row's short
 // last chunk would fall on the same few workgroups every time (all of them when
@@ -621,6 +615,12 @@ __device__ __forceinline__ int64_t claimed_chunk(uint32_t i, int64_t nblk) {
   return o + nblk * int64_t(i);
 }
 
+// The step's token gather (the stream grid's extra, last workgroup): for every
+// (chain, position) the logits at the draft token, read only for sampled rows
+// and valid tokens, and ln u of the accept uniform (Philox counter (0,
+// position, chain, accept purpose)), so that the draws' prologue finds them
+// with one load that depends on nothing. With one workgroup per CU this
+// workgroup starts when the first streaming one ends.
 template <int DT>
 __device__ void gather_tokens(const StreamArgs& a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
