@@ -1401,7 +1401,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void draw_kernel(ChainArgs a) {
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
   __shared__ Top2 s_top[kWavesPerBlock];
-  __shared__ uint32_t s_last;
   __shared__ double s_lnz[kMaxRowsPerChain];
   __shared__ int32_t s_amax[SV_MAX_GAMMA + 1];
   __shared__ int32_t s_rowbad[kRowsPerPass];
@@ -1456,24 +1455,21 @@ void draw_kernel(ChainArgs a) {
   const Top2 wbest = with_logits<DT>(wave_best2(best), row_t, row_d, residual, a.V);
   if (lane == 0) s_top[t / kWave] = wbest;
   __syncthreads();
-  if (t < kWave) {
-    Top2 all = s_top[0];
-    for (int w = 1; w < kWavesPerBlock; ++w) all = top2_merge(all, s_top[w]);
-    const Cand c = rescore_top2(all, residual, double(T), lzt, lzd, dp.pos, dp.r, dp.s0, dp.s1);
-    if (lane == 0) {
-      if (!a.cnt) {
-        a.cand[chain * a.nsplit + split] = c;
-      } else {
-        pub_cand(a.cand + chain * a.nsplit + split, c);
-        stores_done();
-        const uint32_t prev = bump32(a.cnt + chain);
-        s_last = prev == uint32_t(a.nsplit - 1);
-      }
+  if (t >= kWave) return;  // wavefront 0 merges, publishes and, if last, selects
+  Top2 all = s_top[0];
+  for (int w = 1; w < kWavesPerBlock; ++w) all = top2_merge(all, s_top[w]);
+  const Cand c = rescore_top2(all, residual, double(T), lzt, lzd, dp.pos, dp.r, dp.s0, dp.s1);
+  uint32_t prev = 0;
+  if (lane == 0) {
+    if (!a.cnt) {
+      a.cand[chain * a.nsplit + split] = c;
+    } else {
+      pub_cand(a.cand + chain * a.nsplit + split, c);
+      stores_done();
+      prev = bump32(a.cnt + chain);
     }
   }
-  if (!a.cnt) return;
-  __syncthreads();
-  if (!s_last || t >= kWave) return;
+  if (!a.cnt || __builtin_amdgcn_readfirstlane(prev) != uint32_t(a.nsplit - 1)) return;
   // The chain's last split picks the token: the best float64 score over the
   // splits (ties to the lowest id); no candidate anywhere means an empty
   // residual support (rounding only), drawn from p_n with the same noise.
