@@ -601,18 +601,54 @@ struct StreamArgs {
   // The chunk-index divisions (by cpr, P, K*G, G) as multiply-shifts: every
   // chunk index is below 2^31 (the host rejects larger calls).
   FastDiv by_cpr, by_p, by_kg, by_g;
+  float win_scale;  // window_scale of the launch (set with the grid)
 };
 
-// The chunk of a persistent workgroup's i-th claim: chunk nblk*i + ((g + (i
-// mod 32)) mod nblk) for workgroup g of nblk. Without the rotation a row's short
-// last chunk would fall on the same few workgroups every time (all of them when
-// nblk is a multiple of the chunks per row, e.g. 256 workgroups and 32 chunks),
-// which would then idle while the others stream. Chunks rise with i, so a
-// workgroup's first one past the end ends its loop.
-__device__ __forceinline__ int64_t claimed_chunk(uint32_t i, int64_t nblk) {
-  int64_t o = int64_t(blockIdx.x) + int64_t(nblk >= 32 ? (i & 31u) : 0u);
-  if (o >= nblk) o -= nblk;
-  return o + nblk * int64_t(i);
+// The chunk of a persistent workgroup's i-th claim. Claims i < i0 take whole
+// windows of nblk chunks: chunk nblk*i + ((g + (i mod 32)) mod nblk) for
+// workgroup g of nblk. Without the rotation a row's short last chunk would fall
+// on the same few workgroups every time (all of them when nblk is a multiple of
+// the chunks per row, e.g. 256 workgroups and 32 chunks), which would then idle
+// while the others stream. Claims i >= i0 take windows of E = ceil(nblk / 2)
+// chunks shared by the even workgroups alone (rotated the same way): the
+// workgroups are dealt to the 8 XCDs round robin, and the odd XCDs stream ~5%
+// slower than the even ones (device-clock traces: B=512 K=4 gamma=8, even XCDs
+// end at ~816 us, odd ones at ~857 us), so the even ones take the last ~5%.
+// Chunks rise with i, so a workgroup's first one past the end ends its loop
+// (odd workgroups: every claim from i0 on). !TAIL: whole windows only (a
+// separate kernel, as the check alone measured +0.35 us per step at B=64
+// gamma=8 V=128256, where it never applies).
+template <bool TAIL>
+__device__ __forceinline__ int64_t claimed_chunk(uint32_t i, int64_t nblk, uint32_t i0) {
+  if (!TAIL || i < i0) {
+    int64_t o = int64_t(blockIdx.x) + int64_t(nblk >= 32 ? (i & 31u) : 0u);
+    if (o >= nblk) o -= nblk;
+    return o + nblk * int64_t(i);
+  }
+  if (blockIdx.x & 1u) return INT64_MAX;
+  const int64_t E = (nblk + 1) / 2;
+  const uint32_t j = i - i0;
+  int64_t o = int64_t(blockIdx.x / 2u) + int64_t(E >= 32 ? (j & 31u) : 0u);
+  if (o >= E) o -= E;
+  return int64_t(i0) * nblk + o + E * int64_t(j);
+}
+
+// The whole windows before the even workgroups take over, as a factor on the
+// unit count: 1 / (nblk + E/20), so that the even workgroups' extra share is
+// ~5% of theirs; 0 (no such windows) for grids under 64 workgroups, and where a
+// workgroup reads fewer than 192 chunks (12 per wavefront; `chunks` per unit):
+// there the even workgroups' extra chunk per wavefront outlasts the 5% (B=64
+// gamma=8 V=128256, 136 chunks per workgroup: 67.4 vs 66.4 us per step;
+// B=256 gamma=4 V=151936, 260: 121.7 vs 122.8 us; B=512 K=4 gamma=8, 2624:
+// 1112 vs 1125 us). In float32, on the host: a count off by one moves a few
+// chunks between the two kinds of windows, and every count maps the chunks one
+// to one.
+inline float window_scale(int64_t total, int64_t nblk, int64_t chunks) {
+  if (nblk < 64 || total * chunks < 192 * nblk) return 0.0f;
+  return 20.0f / float(20 * nblk + (nblk + 1) / 2);
+}
+__device__ __forceinline__ uint32_t full_windows(int64_t total, float scale) {
+  return scale > 0.0f ? uint32_t(float(uint32_t(total)) * scale) : UINT32_MAX;
 }
 
 // The step's token gather (the stream grid's extra, last workgroup): for every
@@ -645,7 +681,7 @@ __device__ void gather_tokens(const StreamArgs& a) {
 // claim them in order), so at any moment the grid reads one moving window of
 // the rows. A chunk's loads are all issued before any is used. Sampled rows: chunk maximum M and s = sum 2^((z - M) * k2);
 // greedy rows: maximum and lowest argmax; ARGMAX_ALL: argmax of sampled rows too.
-template <int DT, bool VEC, bool ARGMAX_ALL>
+template <int DT, bool VEC, bool ARGMAX_ALL, bool TAIL>
 __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
   __shared__ SampledTable tab;
   __shared__ uint32_t s_claim;
@@ -681,10 +717,11 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
   const int64_t cv = int64_t(kWave) * CL;
   const int64_t total = nrows * a.cpr;
   const bool v_tail = (a.V % kVec) != 0;
+  const uint32_t i0 = TAIL ? full_windows(total, a.win_scale) : UINT32_MAX;
   // the workgroup's wavefronts claim its chunks in order
   uint32_t claim = 0;
   if (lane == 0) claim = atomicAdd(&s_claim, 1u);
-  int64_t c = claimed_chunk(__builtin_amdgcn_readfirstlane(claim), nblk);
+  int64_t c = claimed_chunk<TAIL>(__builtin_amdgcn_readfirstlane(claim), nblk, i0);
   while (c < total) {
     uint32_t next = 0;
     if (lane == 0) next = atomicAdd(&s_claim, 1u);  // the next claim, answered during the loads
@@ -796,7 +833,7 @@ __global__ __launch_bounds__(kStreamBlock) void stream_kernel(StreamArgs a) {
       }
     }
     if (lane == 0 && unit_ok) a.part[slot * a.cpr + (c - rho * a.cpr)] = out;
-    c = claimed_chunk(__builtin_amdgcn_readfirstlane(next), nblk);
+    c = claimed_chunk<TAIL>(__builtin_amdgcn_readfirstlane(next), nblk, i0);
   }
 }
 
@@ -1578,6 +1615,7 @@ struct OverlapArgs {
   const double* lnz_d;     // [B, K, G]
   OverlapPartial* part;    // [(b*K + k)*G + j][cpr]
   FastDiv by_cpr, by_g;    // unit indices are below 2^31 (checked on the host)
+  float win_scale;         // window_scale of the launch (set with the grid)
 };
 
 // One sweep over the target rows 0..G-1 and every draft row. A unit is
@@ -1590,7 +1628,7 @@ struct OverlapArgs {
 // term, so the float32 exponent carries no cancellation error where the terms
 // are large; per-vector sums in float32, lane sums in float64. Persistent: one workgroup per CU claiming
 // units from an LDS counter.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool TAIL>
 __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
   __shared__ uint32_t s_claim;
   constexpr int CL = chunk_lanes<DT>();
@@ -1604,9 +1642,10 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
   const int64_t nblk = gridDim.x;
   const bool v_tail = (a.V % kVec) != 0;
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  const uint32_t i0 = TAIL ? full_windows(total, a.win_scale) : UINT32_MAX;
   uint32_t claim = 0;
   if (lane == 0) claim = atomicAdd(&s_claim, 1u);
-  int64_t c = claimed_chunk(__builtin_amdgcn_readfirstlane(claim), nblk);
+  int64_t c = claimed_chunk<TAIL>(__builtin_amdgcn_readfirstlane(claim), nblk, i0);
   while (c < total) {
     uint32_t next = 0;
     if (lane == 0) next = atomicAdd(&s_claim, 1u);
@@ -1617,7 +1656,7 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
     const int64_t v0 = chunk * cv;
     const int64_t v1 = v0 + cv < a.vpr ? v0 + cv : a.vpr;
     if (!sv_ok(b < rs.B && j < G && chunk < a.cpr && v0 < v1)) {
-      c = claimed_chunk(__builtin_amdgcn_readfirstlane(next), nblk);
+      c = claimed_chunk<TAIL>(__builtin_amdgcn_readfirstlane(next), nblk, i0);
       continue;
     }
     const float T = rs.temp[b];
@@ -1729,7 +1768,7 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
       }
       if (lane == 0) a.part[(chain * G + j) * a.cpr + chunk] = out;
     }
-    c = claimed_chunk(__builtin_amdgcn_readfirstlane(next), nblk);
+    c = claimed_chunk<TAIL>(__builtin_amdgcn_readfirstlane(next), nblk, i0);
   }
 }
 
@@ -2296,7 +2335,7 @@ int64_t stream_blocks() {
       cus <= 0)
     cus = 256;
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<DT, VEC, ARGMAX_ALL>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, stream_kernel<DT, VEC, ARGMAX_ALL, false>,
                                                    kStreamBlock, 0) != hipSuccess ||
       blocks <= 0)
     blocks = 1;
@@ -2315,17 +2354,18 @@ int launch_status() { return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP; 
 // start and end (hipExtLaunchKernel), so their elapsed time is the kernel's
 // execution alone, as a profiler reports it.
 template <int DT, bool VEC, bool ARGMAX_ALL>
-void launch_stream_t(const StreamArgs& sa, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+void launch_stream_t(StreamArgs sa, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   int64_t grid = stream_blocks<DT, VEC, ARGMAX_ALL>();
   const int64_t need = (sa.nrows * sa.cpr + kStreamWaves - 1) / kStreamWaves;
   if (grid > need) grid = need;
+  sa.win_scale = window_scale(sa.nrows * sa.cpr, grid, 1);  // compact mode: the all-sampled bound
   if (sa.tok_aux) grid += 1;  // the token gather
+  auto kernel = sa.win_scale > 0.0f ? stream_kernel<DT, VEC, ARGMAX_ALL, true>
+                                    : stream_kernel<DT, VEC, ARGMAX_ALL, false>;
   if (ev0)
-    hipExtLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(grid)),
-                          dim3(kStreamBlock), 0, st, ev0, ev1, 0u, sa);
+    hipExtLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kStreamBlock), 0, st, ev0, ev1, 0u, sa);
   else
-    hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL>), dim3(unsigned(grid)),
-                       dim3(kStreamBlock), 0, st, sa);
+    hipLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kStreamBlock), 0, st, sa);
 }
 
 void launch_stream_dt(int dtype, bool vec, bool argmax_all, const StreamArgs& sa, hipStream_t st,
@@ -2523,7 +2563,7 @@ int64_t overlap_blocks() {
       cus <= 0)
     cus = 256;
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, overlap_kernel<DT, VEC>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, overlap_kernel<DT, VEC, false>,
                                                    kStreamBlock, 0) != hipSuccess ||
       blocks <= 0)
     blocks = 1;
@@ -2533,12 +2573,13 @@ int64_t overlap_blocks() {
 }
 
 template <int DT, bool VEC>
-void launch_overlap(const OverlapArgs& oa, int64_t units, hipStream_t st) {
+void launch_overlap(OverlapArgs oa, int64_t units, hipStream_t st) {
   int64_t grid = overlap_blocks<DT, VEC>();
   const int64_t need = (units + kStreamWaves - 1) / kStreamWaves;
   if (grid > need) grid = need;
-  hipLaunchKernelGGL((overlap_kernel<DT, VEC>), dim3(unsigned(grid)), dim3(kStreamBlock), 0, st,
-                     oa);
+  oa.win_scale = window_scale(units, grid, 1 + oa.rs.K);  // a unit: a target chunk, K draft
+  auto kernel = oa.win_scale > 0.0f ? overlap_kernel<DT, VEC, true> : overlap_kernel<DT, VEC, false>;
+  hipLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kStreamBlock), 0, st, oa);
 }
 
 // Outcome fan-out (host array [G+1]) into the kernel arguments; false if any
