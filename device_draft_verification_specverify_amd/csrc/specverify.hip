@@ -1817,9 +1817,13 @@ __global__ __launch_bounds__(kBlock) void alpha_law_kernel(const OverlapPartial*
 #pragma unroll
     for (int q = 0; q < kAlphaBatch; ++q) {
       if (j0 + q >= G) break;  // uniform
-      s[q] = wave_sum(s[q]);
-      wave_argmax(tm[q], ti[q]);
-      wave_argmax(dm[q], di[q]);
+      // a sampled chain needs the sum alone, a greedy one the two argmaxes alone
+      if (sampled) {
+        s[q] = wave_sum(s[q]);
+      } else if (greedy) {
+        wave_argmax(tm[q], ti[q]);
+        wave_argmax(dm[q], di[q]);
+      }
       const int64_t j = j0 + q;
       const double aj = sampled ? s[q] : greedy ? (ti[q] == di[q] ? 1.0 : 0.0) : double(NAN);
       if (lane == 0) {
