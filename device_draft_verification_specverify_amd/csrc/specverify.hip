@@ -642,7 +642,8 @@ __device__ __forceinline__ int64_t claimed_chunk(uint32_t i, int64_t nblk, uint3
 // B=256 gamma=4 V=151936, 260: 121.7 vs 122.8 us; B=512 K=4 gamma=8, 2624:
 // 1112 vs 1125 us). In float32, on the host: a count off by one moves a few
 // chunks between the two kinds of windows, and every count maps the chunks one
-// to one.
+// to one. The stream kernel uses it (the overlap sweep of the acceptance
+// probability claims whole windows only).
 inline float window_scale(int64_t total, int64_t nblk, int64_t chunks) {
   if (nblk < 64 || total * chunks < 192 * nblk) return 0.0f;
   return 20.0f / float(20 * nblk + (nblk + 1) / 2);
@@ -1615,7 +1616,6 @@ struct OverlapArgs {
   const double* lnz_d;     // [B, K, G]
   OverlapPartial* part;    // [(b*K + k)*G + j][cpr]
   FastDiv by_cpr, by_g;    // unit indices are below 2^31 (checked on the host)
-  float win_scale;         // window_scale of the launch (set with the grid)
 };
 
 // One sweep over the target rows 0..G-1 and every draft row. A unit is
@@ -1628,7 +1628,7 @@ struct OverlapArgs {
 // term, so the float32 exponent carries no cancellation error where the terms
 // are large; per-vector sums in float32, lane sums in float64. Persistent: one workgroup per CU claiming
 // units from an LDS counter.
-template <int DT, bool VEC, bool TAIL>
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
   __shared__ uint32_t s_claim;
   constexpr int CL = chunk_lanes<DT>();
@@ -1642,10 +1642,12 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
   const int64_t nblk = gridDim.x;
   const bool v_tail = (a.V % kVec) != 0;
   constexpr int esz = DT == SV_BF16 ? 2 : 4;
-  const uint32_t i0 = TAIL ? full_windows(total, a.win_scale) : UINT32_MAX;
+  // whole windows only: the even XCDs' tail windows measured mixed here
+  // (B=256 gamma=4 V=151936: 104.7 vs 105.7 us; B=512 K=4 gamma=8: 938 vs 931)
+  const uint32_t i0 = UINT32_MAX;
   uint32_t claim = 0;
   if (lane == 0) claim = atomicAdd(&s_claim, 1u);
-  int64_t c = claimed_chunk<TAIL>(__builtin_amdgcn_readfirstlane(claim), nblk, i0);
+  int64_t c = claimed_chunk<false>(__builtin_amdgcn_readfirstlane(claim), nblk, i0);
   while (c < total) {
     uint32_t next = 0;
     if (lane == 0) next = atomicAdd(&s_claim, 1u);
@@ -1656,7 +1658,7 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
     const int64_t v0 = chunk * cv;
     const int64_t v1 = v0 + cv < a.vpr ? v0 + cv : a.vpr;
     if (!sv_ok(b < rs.B && j < G && chunk < a.cpr && v0 < v1)) {
-      c = claimed_chunk<TAIL>(__builtin_amdgcn_readfirstlane(next), nblk, i0);
+      c = claimed_chunk<false>(__builtin_amdgcn_readfirstlane(next), nblk, i0);
       continue;
     }
     const float T = rs.temp[b];
@@ -1768,7 +1770,7 @@ __global__ __launch_bounds__(kStreamBlock) void overlap_kernel(OverlapArgs a) {
       }
       if (lane == 0) a.part[(chain * G + j) * a.cpr + chunk] = out;
     }
-    c = claimed_chunk<TAIL>(__builtin_amdgcn_readfirstlane(next), nblk, i0);
+    c = claimed_chunk<false>(__builtin_amdgcn_readfirstlane(next), nblk, i0);
   }
 }
 
@@ -2567,7 +2569,7 @@ int64_t overlap_blocks() {
       cus <= 0)
     cus = 256;
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, overlap_kernel<DT, VEC, false>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, overlap_kernel<DT, VEC>,
                                                    kStreamBlock, 0) != hipSuccess ||
       blocks <= 0)
     blocks = 1;
@@ -2577,13 +2579,12 @@ int64_t overlap_blocks() {
 }
 
 template <int DT, bool VEC>
-void launch_overlap(OverlapArgs oa, int64_t units, hipStream_t st) {
+void launch_overlap(const OverlapArgs& oa, int64_t units, hipStream_t st) {
   int64_t grid = overlap_blocks<DT, VEC>();
   const int64_t need = (units + kStreamWaves - 1) / kStreamWaves;
   if (grid > need) grid = need;
-  oa.win_scale = window_scale(units, grid, 1 + oa.rs.K);  // a unit: a target chunk, K draft
-  auto kernel = oa.win_scale > 0.0f ? overlap_kernel<DT, VEC, true> : overlap_kernel<DT, VEC, false>;
-  hipLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kStreamBlock), 0, st, oa);
+  hipLaunchKernelGGL((overlap_kernel<DT, VEC>), dim3(unsigned(grid)), dim3(kStreamBlock), 0, st,
+                     oa);
 }
 
 // Outcome fan-out (host array [G+1]) into the kernel arguments; false if any
