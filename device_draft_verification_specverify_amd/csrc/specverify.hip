@@ -1340,13 +1340,31 @@ __device__ void chain_prologue(const ChainArgs& a, int64_t chain, bool lead, dou
         const int64_t c = c0 + int64_t(u) * kRowLanes;
         q[u] = (has && c < a.cpr) ? a.part[rho * a.cpr + c] : RowPartial{-INFINITY, INT_MAX, 0.0};
       }
+      // a sampled row needs the maximum alone (the same value), a greedy one
+      // its lowest argmax too
+      if (sampled) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) fold_partial(m, idx, s, q[u], sampled, k2);
+        for (int u = 0; u < 4; ++u) {
+          const float bm = fmaxf(m, q[u].m);
+          if (bm > -INFINITY && m > -INFINITY) s *= exp2_scale((double(m) - double(bm)) * k2);
+          s += q[u].m > -INFINITY ? q[u].s * exp2_scale((double(q[u].m) - double(bm)) * k2) : q[u].s;
+          m = bm;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) fold_partial(m, idx, s, q[u], sampled, k2);
+      }
     }
     // combine the 8 lanes of each row in a fixed order
     float M = m;
     int32_t I = idx;
-    group8_argmax(M, I);
+    if (sampled) {
+      M = fmaxf(M, __uint_as_float(dpp32<kDppXor1>(__float_as_uint(M))));
+      M = fmaxf(M, __uint_as_float(dpp32<kDppXor2>(__float_as_uint(M))));
+      M = fmaxf(M, __uint_as_float(dpp32<kDppHalfMirror>(__float_as_uint(M))));
+    } else {
+      group8_argmax(M, I);
+    }
     double sr = (sampled && M > -INFINITY && m > -INFINITY) ? s * exp2_scale((double(m) - double(M)) * k2) : s;
     sr = group8_sum(sr);
     if (has && gl == 0) {
