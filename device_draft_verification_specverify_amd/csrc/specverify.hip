@@ -2384,12 +2384,23 @@ void launch_stream_t(StreamArgs sa, hipStream_t st, hipEvent_t ev0, hipEvent_t e
   if (grid > need) grid = need;
   sa.win_scale = window_scale(sa.nrows * sa.cpr, grid, 1);  // compact mode: the all-sampled bound
   if (sa.tok_aux) grid += 1;  // the token gather
-  auto kernel = sa.win_scale > 0.0f ? stream_kernel<DT, VEC, ARGMAX_ALL, true>
-                                    : stream_kernel<DT, VEC, ARGMAX_ALL, false>;
-  if (ev0)
-    hipExtLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kStreamBlock), 0, st, ev0, ev1, 0u, sa);
-  else
-    hipLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(kStreamBlock), 0, st, sa);
+  // direct launches (a kernel picked through a function pointer is an
+  // indirect call, which function-type sanitizers instrument)
+  if (sa.win_scale > 0.0f) {
+    if (ev0)
+      hipExtLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL, true>), dim3(unsigned(grid)),
+                            dim3(kStreamBlock), 0, st, ev0, ev1, 0u, sa);
+    else
+      hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL, true>), dim3(unsigned(grid)),
+                         dim3(kStreamBlock), 0, st, sa);
+  } else {
+    if (ev0)
+      hipExtLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL, false>), dim3(unsigned(grid)),
+                            dim3(kStreamBlock), 0, st, ev0, ev1, 0u, sa);
+    else
+      hipLaunchKernelGGL((stream_kernel<DT, VEC, ARGMAX_ALL, false>), dim3(unsigned(grid)),
+                         dim3(kStreamBlock), 0, st, sa);
+  }
 }
 
 void launch_stream_dt(int dtype, bool vec, bool argmax_all, const StreamArgs& sa, hipStream_t st,
