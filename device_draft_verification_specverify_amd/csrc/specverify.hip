@@ -1128,8 +1128,8 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
 // 8, else all but the row's last), the loads are issued unconditionally (lanes
 // past the row load the row's last vector and never score it) and the scoring
 // is unrolled, so vector it waits only for its own loads and the arithmetic of
-// the first vectors overlaps the arrival of the later ones. FILTER: after each
-// vector the wavefront's smallest second-best key bounds the ids worth scoring
+// the first vectors overlaps the arrival of the later ones. FILTER: after every
+// other vector the wavefront's smallest second-best key bounds the ids worth scoring
 // (score_vec_filtered); it pays where the draws are bound by arithmetic (grids
 // of several rounds) and costs latency where a single round of workgroups is
 // bound by its dependent steps.
@@ -1158,7 +1158,10 @@ __device__ __forceinline__ Best2 scan_split(const void* row_t, const void* row_d
         const int64_t vi = vi0 + int64_t(kWave) * it;
         if (vi < vpr)
           score_vec_filtered<DT, RESIDUAL>(wt[it], RESIDUAL ? wd[it] : wt[it], vi, dp, thr, best);
-        thr = wave_min(cand_key(best.c2));
+        // after every other vector: an older bound is still a bound, and the
+        // reduction costs more than the tighter one saves (B=512 K=4 gamma=8:
+        // 1113.5 vs 1116.9 us per step; every vector or every fourth: no better)
+        if ((it & 1) == 0 && it + 1 < SI) thr = wave_min(cand_key(best.c2));
       }
     } else {
 #pragma unroll
