@@ -1102,7 +1102,10 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
       const Philox4 blk = philox4x32_10(uint32_t(v) >> 2, pos, r, kPurposeSample, s0, s1);
       const uint32_t k = uint32_t(v) & 3u;
       const uint32_t word = k == 0u ? blk.w[0] : k == 1u ? blk.w[1] : k == 2u ? blk.w[2] : blk.w[3];
-      y = -log_uniform_d(unit_uniform_d(word));
+      // u - 1 is exact for every u here ((k + 1/2) 2^-23: 24 significant
+      // bits), so log1p keeps full accuracy over the whole range and both
+      // lanes take one path (B=256 gamma=4 V=151936: 119.9 vs 120.3 us)
+      y = -log1p(unit_uniform_d(word) - 1.0);
     } else {
       lp = double(second ? all.t2 : all.t1) / T - lzt;
       if (residual) {
