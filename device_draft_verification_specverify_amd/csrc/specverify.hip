@@ -1145,9 +1145,10 @@ __device__ __forceinline__ Cand rescore_top2(const Top2& all, bool residual, dou
 // (score_vec_filtered); it pays where the draws are bound by arithmetic (grids
 // of several rounds) and costs latency where a single round of workgroups is
 // bound by its dependent steps.
-template <int DT, bool VEC, bool RESIDUAL, bool FILTER, int SI>
+template <int DT, bool VEC, bool RESIDUAL, bool FILTER, int SI, bool ACC = false>
 __device__ __forceinline__ Best2 scan_split(const void* row_t, const void* row_d, int64_t split,
-                                           int64_t V, const DrawParams& dp) {
+                                           int64_t V, const DrawParams& dp,
+                                           const Best2& init = best2_empty()) {
   constexpr int64_t kSplitVecs = int64_t(kBlock) * SI;  // vectors per split
   const int64_t vpr = (V + kVec - 1) / kVec;
   const int64_t vi0 = split * kSplitVecs +
@@ -1162,9 +1163,10 @@ __device__ __forceinline__ Best2 scan_split(const void* row_t, const void* row_d
       wt[it] = load_vec<DT, true>(row_t, vc);
       if constexpr (RESIDUAL) wd[it] = load_vec<DT, true>(row_d, vc);
     }
-    Best2 best = best2_empty();
+    Best2 best = ACC ? init : best2_empty();
     if constexpr (FILTER) {
-      float thr = INFINITY;  // two keys of one lane are at most thr
+      // two keys of one lane are at most thr (ACC: the earlier splits' too)
+      float thr = ACC ? wave_min(cand_key(best.c2)) : INFINITY;
 #pragma unroll
       for (int it = 0; it < SI; ++it) {
         const int64_t vi = vi0 + int64_t(kWave) * it;
@@ -1192,7 +1194,7 @@ __device__ __forceinline__ Best2 scan_split(const void* row_t, const void* row_d
     rt[it] = inside ? load_vec_bounded<DT, VEC>(row_t, vi, V) : neg_inf_vec<DT>();
     rd[it] = inside && RESIDUAL ? load_vec_bounded<DT, VEC>(row_d, vi, V) : rt[it];
   }
-  Best2 best = best2_empty();
+  Best2 best = ACC ? init : best2_empty();
 #pragma unroll 1
   for (int it = 0; it < SI; ++it) {
     const int64_t vi = vi0 + int64_t(kWave) * it;
@@ -1554,6 +1556,58 @@ void draw_kernel(ChainArgs a) {
     }
   }
   wave_best_cand(bs, id);
+  if (id == INT_MAX) id = draw_from_p<DT, VEC>(row_t, a.V, double(T), lzt, dp);
+  if (lane == 0) a.out_token[chain] = id == INT_MAX ? -1 : id;
+}
+
+// Grids of many chains (after accept_kernel): one workgroup per chain scans
+// the chain's whole row pair, split after split, keeping every lane's best two
+// (and the filter's bound) across the splits, then merges and re-scores them
+// once; no other workgroup takes part, so nothing is handed over.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void draw_chain_kernel(ChainArgs a) {
+  constexpr int esz = DT == SV_BF16 ? 2 : 4;
+  __shared__ Top2 s_top[kWavesPerBlock];
+  const RowSet& rs = a.rs;
+  const int64_t chain = blockIdx.x;
+  const ChainInfo ci = a.info[chain];
+  const int n = ci.n;
+  const int G = int(rs.G);
+  if (n < 0) return;  // uniform: this chain draws nothing
+  if (!sv_ok(n <= G && chain < rs.B * rs.K)) return;
+  const int64_t b = int64_t(fast_div(uint32_t(chain), a.by_k));
+  const int64_t k = chain - b * rs.K;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const float T = rs.temp[b];
+  const bool residual = n < G;
+  const void* row_t = row_ptr(rs.t, esz, b * rs.tsb + int64_t(n) * rs.tsj);
+  const void* row_d =
+      residual ? row_ptr(rs.d, esz, b * rs.dsb + k * rs.dsk + int64_t(n) * rs.dsj) : row_t;
+  const double lzt = ci.lzt;
+  const double lzd = residual ? ci.lzd : 0.0;
+  DrawParams dp;
+  dp.k2 = kLog2e / T;
+  dp.L2t = float(lzt * kLog2eD);
+  dp.D2 = residual ? float((lzt - lzd) * kLog2eD) : 0.0f;
+  dp.pos = uint32_t(uint64_t(a.pos0 ? a.pos0[b] : 0) + uint64_t(n));
+  dp.r = uint32_t(chain);
+  dp.s0 = uint32_t(a.seed);
+  dp.s1 = uint32_t(a.seed >> 32);
+  const int64_t nsplit = (a.V + kSplit - 1) / kSplit;
+  Best2 best = best2_empty();
+  for (int64_t sp = 0; sp < nsplit; ++sp)
+    best = residual ? scan_split<DT, VEC, true, true, kSampleIters, true>(row_t, row_d, sp, a.V, dp, best)
+                    : scan_split<DT, VEC, false, true, kSampleIters, true>(row_t, row_d, sp, a.V, dp, best);
+  const Top2 wbest = with_logits<DT>(wave_best2(best), row_t, row_d, residual, a.V);
+  if (lane == 0) s_top[t / kWave] = wbest;
+  __syncthreads();
+  if (t >= kWave) return;
+  Top2 all = s_top[0];
+  for (int w = 1; w < kWavesPerBlock; ++w) all = top2_merge(all, s_top[w]);
+  const Cand c = rescore_top2(all, residual, double(T), lzt, lzd, dp.pos, dp.r, dp.s0, dp.s1);
+  int32_t id = c.score == -INFINITY ? INT_MAX : c.id;
   if (id == INT_MAX) id = draw_from_p<DT, VEC>(row_t, a.V, double(T), lzt, dp);
   if (lane == 0) a.out_token[chain] = id == INT_MAX ? -1 : id;
 }
@@ -2482,6 +2536,9 @@ int64_t draw_resident() {
 // is a small part of the whole. B=512 K=4 gamma=8 (25 rounds): 1198 vs 1228 us
 // per step; B=256 K=1 gamma=4 (4 rounds) measured slower this way (137 vs 131).
 constexpr int64_t kWideRounds = 8;
+// From this many chains per CU, one workgroup per chain scans the whole row
+// pair (draw_chain_kernel) instead of one per split.
+constexpr int64_t kChainsPerCuWhole = 4;
 
 template <int DT, bool VEC>
 void launch_chain_finish(ChainArgs ca, bool given, hipStream_t st) {
@@ -2534,6 +2591,10 @@ void launch_chain_finish(ChainArgs ca, bool given, hipStream_t st) {
   } else {
     // more workgroups than fit at once: n per chain in its own launch
     hipLaunchKernelGGL((accept_kernel<DT>), dim3(unsigned(chains)), dim3(kBlock), 0, st, ca);
+    if (chains >= kChainsPerCuWhole * device_cus()) {
+      hipLaunchKernelGGL((draw_chain_kernel<DT, VEC>), dim3(unsigned(chains)), dim3(kBlock), 0, st, ca);
+      return;
+    }
     draws();
   }
   if (ca.cnt) return;  // the chains' last splits picked the tokens
